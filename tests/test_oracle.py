@@ -1,0 +1,338 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: central finite differences,
+automatic differentiation, a singular-value closed form, a library convolution,
+hand-computed closed forms, or a structural property the pages state (additivity
+of the gradient over tokens, the lr = 0 identity, streaming = sequential calls).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import rel_fro
+
+
+def _weights(rng, H, d, m, scale):
+    return (rng.normal(0, scale, (H, m, d)), rng.normal(0, scale, (H, m, d)),
+            rng.normal(0, scale, (H, d, m)))
+
+
+# --------------------------------------------------------------------------- f_W
+def test_swiglu_scalar_closed_form():
+    # d = m = 1: f(x) = w2 * SiLU(w1 x) * (w3 x); SiLU(2) = 2 / (1 + e^-2).
+    w1, w3, w2 = np.array([[2.0]]), np.array([[3.0]]), np.array([[0.5]])
+    f = oracle.swiglu(w1, w3, w2, np.array([[1.0]]))
+    assert f[0, 0] == pytest.approx(0.5 * (2.0 / (1.0 + math.exp(-2.0))) * 3.0, rel=1e-15)
+    assert oracle.silu(np.array(1.0)) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+
+
+def test_swiglu_identity_weights_reduce_to_library_silu(rng):
+    # W1 = W3 = W2 = I gives f(x) = SiLU(x) o x; torch's SiLU is the library routine.
+    d = 12
+    eye = np.eye(d)
+    x = rng.normal(0, 2, (30, d))
+    ref = (torch.nn.functional.silu(torch.from_numpy(x)) * torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(oracle.swiglu(eye, eye, eye, x), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_swiglu_roles_of_w1_w3_w2(rng):
+    d, m = 5, 7
+    w1, w3, w2 = (x[0] for x in _weights(rng, 1, d, m, 0.7))
+    x = rng.normal(0, 1, (9, d))
+    f = oracle.swiglu(w1, w3, w2, x)
+    # linear in W2 and in W3, not in W1; zero W1 gives zero output (SiLU(0) = 0)
+    np.testing.assert_allclose(oracle.swiglu(w1, w3, 2.5 * w2, x), 2.5 * f, rtol=1e-13)
+    np.testing.assert_allclose(oracle.swiglu(w1, -3.0 * w3, w2, x), -3.0 * f, rtol=1e-13)
+    assert np.abs(oracle.swiglu(2.0 * w1, w3, w2, x) - 2.0 * f).max() > 1e-3
+    assert np.all(oracle.swiglu(np.zeros_like(w1), w3, w2, x) == 0.0)
+    # one-hot hidden unit j: f(x) = W2[:, j] * SiLU(w1_j . x) * (w3_j . x)
+    j = 3
+    mask = np.zeros(m)
+    mask[j] = 1.0
+    fj = oracle.swiglu(w1, w3, w2 * mask[None, :], x)
+    z1, z3 = x @ w1[j], x @ w3[j]
+    ref = (z1 / (1 + np.exp(-z1)) * z3)[:, None] * w2[:, j][None, :]
+    np.testing.assert_allclose(fj, ref, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------- gradient
+def test_gradient_matches_central_finite_differences(rng):
+    H, d, m, n = 1, 4, 8, 6
+    w1, w3, w2 = (x[0] for x in _weights(rng, H, d, m, 0.6))
+    k = rng.normal(0, 1, (n, d))
+    v = rng.normal(0, 1, (n, d))
+    eta = rng.uniform(0, 0.1, n)
+    g = oracle.gradient(w1, w3, w2, k, v, eta)
+    h = 1e-6
+    for which, (w, gw) in enumerate(zip((w1, w3, w2), g)):
+        fd = np.zeros_like(w)
+        for idx in np.ndindex(*w.shape):
+            wp, wm = w.copy(), w.copy()
+            wp[idx] += h
+            wm[idx] -= h
+            args_p = [w1, w3, w2]
+            args_m = [w1, w3, w2]
+            args_p[which] = wp
+            args_m[which] = wm
+            fd[idx] = (oracle.dot_product_loss(*args_p, k, v, eta)
+                       - oracle.dot_product_loss(*args_m, k, v, eta)) / (2 * h)
+        assert rel_fro(gw, fd) <= 1e-6, which
+        np.testing.assert_allclose(gw, fd, rtol=1e-5, atol=1e-9)
+
+
+def test_gradient_matches_autograd(rng):
+    # torch autograd differentiates the loss definition independently of the
+    # oracle's hand-written chain rule.
+    H, d, m, n = 1, 16, 32, 50
+    w1, w3, w2 = (x[0] for x in _weights(rng, H, d, m, 0.3))
+    k = rng.normal(0, 1, (n, d))
+    v = rng.normal(0, 1, (n, d))
+    eta = rng.uniform(0, 0.1, n)
+    t = [torch.tensor(x, requires_grad=True) for x in (w1, w3, w2)]
+    kt, vt, et = map(torch.from_numpy, (k, v, eta))
+    f = (torch.nn.functional.silu(kt @ t[0].T) * (kt @ t[1].T)) @ t[2].T
+    loss = -(et * (f * vt).sum(1)).sum()
+    loss.backward()
+    g = oracle.gradient(w1, w3, w2, k, v, eta)
+    for gj, tj in zip(g, t):
+        assert rel_fro(gj, tj.grad.numpy()) <= 1e-12
+    assert oracle.dot_product_loss(w1, w3, w2, k, v, eta) == pytest.approx(loss.item(), rel=1e-12)
+
+
+def test_gradient_is_linear_in_eta_and_zero_at_eta_zero(rng):
+    d, m, n = 8, 16, 40
+    w = [x[0] for x in _weights(rng, 1, d, m, 0.2)]
+    k = rng.normal(0, 1, (n, d))
+    v = rng.normal(0, 1, (n, d))
+    ea, eb = rng.uniform(0, 0.1, n), rng.uniform(0, 0.1, n)
+    ga = oracle.gradient(*w, k, v, ea)
+    gb = oracle.gradient(*w, k, v, eb)
+    gab = oracle.gradient(*w, k, v, ea + eb)
+    g3 = oracle.gradient(*w, k, v, 3.0 * ea)
+    for j in range(3):
+        assert rel_fro(gab[j], ga[j] + gb[j]) <= 1e-12
+        assert rel_fro(g3[j], 3.0 * ga[j]) <= 1e-12
+        assert np.all(oracle.gradient(*w, k, v, np.zeros(n))[j] == 0.0)
+
+
+def test_gradient_additive_over_token_partitions_and_order_free(rng):
+    # Scal3R 方案2 / VGG-T3 关键发现 2: the gradient is a sum over token subsets.
+    d, m, n = 8, 16, 90
+    w = [x[0] for x in _weights(rng, 1, d, m, 0.2)]
+    k = rng.normal(0, 1, (n, d))
+    v = rng.normal(0, 1, (n, d))
+    eta = rng.uniform(0, 0.1, n)
+    g = oracle.gradient(*w, k, v, eta)
+    cut = 37
+    ga = oracle.gradient(*w, k[:cut], v[:cut], eta[:cut])
+    gb = oracle.gradient(*w, k[cut:], v[cut:], eta[cut:])
+    p = rng.permutation(n)
+    gp = oracle.gradient(*w, k[p], v[p], eta[p])
+    for j in range(3):
+        assert rel_fro(g[j], ga[j] + gb[j]) <= 1e-12
+        assert rel_fro(g[j], gp[j]) <= 1e-12
+
+
+def test_gradient_step_descends_the_loss(rng):
+    d, m, n = 8, 16, 60
+    w = [x[0] for x in _weights(rng, 1, d, m, 0.2)]
+    k = rng.normal(0, 1, (n, d))
+    v = rng.normal(0, 1, (n, d))
+    eta = rng.uniform(0, 0.1, n)
+    g = oracle.gradient(*w, k, v, eta)
+    ns = [oracle.newton_schulz(x) for x in g]
+    base = oracle.dot_product_loss(*w, k, v, eta)
+    lr = 1e-3
+    assert oracle.dot_product_loss(*[a - lr * b for a, b in zip(w, g)], k, v, eta) < base
+    assert oracle.dot_product_loss(*[a - lr * b for a, b in zip(w, ns)], k, v, eta) < base
+    for gj, nj in zip(g, ns):
+        assert np.sum(gj * nj) > 0.0
+
+
+# ------------------------------------------------------------------ Newton-Schulz
+def _p5(x):
+    # Muon's quintic map applied five times, written from its coefficients.
+    for _ in range(5):
+        x = 3.4445 * x - 4.7750 * x ** 3 + 2.0315 * x ** 5
+    return x
+
+
+@pytest.mark.parametrize("shape", [(24, 40), (40, 24), (32, 32), (3, 50)])
+def test_newton_schulz_svd_closed_form(rng, shape):
+    g = rng.normal(0, 1, shape)
+    u, s, vt = np.linalg.svd(g, full_matrices=False)
+    ref = u @ np.diag(_p5(s / (np.linalg.norm(g) + 1e-7))) @ vt
+    assert rel_fro(oracle.newton_schulz(g), ref) <= 1e-10
+
+
+def test_newton_schulz_singular_value_band(rng):
+    # For normalised singular values in [1.5e-3, 1] the five quintic steps land in
+    # [0.6798, 1.2024] (the band Muon's coefficients are tuned for).
+    xs = np.logspace(np.log10(1.5e-3), 0, 20001)
+    ys = _p5(xs)
+    assert ys.min() >= 0.6798 and ys.max() <= 1.2024
+    g = rng.normal(0, 1, (64, 128))
+    sx = np.linalg.svd(g, compute_uv=False) / np.linalg.norm(g)
+    assert sx.min() > 1.5e-3
+    sy = np.linalg.svd(oracle.newton_schulz(g), compute_uv=False)
+    assert sy.min() >= 0.6798 and sy.max() <= 1.2024
+
+
+def test_newton_schulz_equal_singular_values(rng):
+    r, c = 16, 40
+    q, _ = np.linalg.qr(rng.normal(0, 1, (c, r)))
+    g = 2.5 * q.T                      # r x c with all singular values 2.5
+    x = 2.5 / (2.5 * math.sqrt(r) + 1e-7)
+    np.testing.assert_allclose(oracle.newton_schulz(g), _p5(x) * q.T, rtol=1e-11, atol=1e-13)
+
+
+def test_newton_schulz_symmetries(rng):
+    g = rng.normal(0, 1, (20, 36))
+    ns = oracle.newton_schulz(g)
+    assert np.array_equal(oracle.newton_schulz(-g), -ns)
+    assert np.array_equal(oracle.newton_schulz(g.T), ns.T)
+    assert rel_fro(oracle.newton_schulz(7.3 * g), ns) <= 1e-6
+    assert np.all(oracle.newton_schulz(np.zeros((8, 12))) == 0.0)
+
+
+# ----------------------------------------------------------------- update/apply
+def _layer_inputs(rng, H, d, m, n, nq, scale=0.02):
+    w = _weights(rng, H, d, m, scale)
+    k = rng.normal(0, 1, (n, H * d))
+    k /= np.linalg.norm(k.reshape(n, H, d), axis=2).repeat(d, axis=1)
+    v = rng.normal(0, 1, (n, H * d))
+    q = rng.normal(0, 1, (nq, H * d))
+    eta = rng.uniform(0, 0.1, (H, n))
+    return w, k, v, q, eta
+
+
+def test_lr_zero_leaves_w_and_apply_is_f_w0(rng):
+    w, k, v, q, eta = _layer_inputs(rng, 2, 8, 16, 50, 30)
+    w_hat, g, ns = oracle.update(*w, k, v, eta, lr=0.0, steps=1)
+    for a, b in zip(w_hat, w):
+        assert np.array_equal(a, b)
+    o = oracle.apply(*w_hat, q)
+    for h in range(2):
+        c = slice(8 * h, 8 * h + 8)
+        for i in range(q.shape[0]):          # per-token loop of f_W0
+            x = q[i, c]
+            z1, z3 = w[0][h] @ x, w[1][h] @ x
+            ref = w[2][h] @ (z1 / (1.0 + np.exp(-z1)) * z3)
+            np.testing.assert_allclose(o[i, c], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_step_is_lr_times_ns_and_two_steps_compose(rng):
+    w, k, v, q, eta = _layer_inputs(rng, 2, 8, 16, 50, 30, scale=0.3)
+    lr = 0.05
+    w1s, g, ns = oracle.update(*w, k, v, eta, lr=lr, steps=1)
+    for a, b, n_ in zip(w, w1s, ns):
+        assert rel_fro((a - b) / lr, n_) <= 1e-12
+    w2s, _, _ = oracle.update(*w, k, v, eta, lr=lr, steps=2)
+    w2b, _, _ = oracle.update(*w1s, k, v, eta, lr=lr, steps=1)
+    for a, b in zip(w2s, w2b):
+        assert np.array_equal(a, b)
+
+
+def test_heads_are_independent(rng):
+    H, d, m, n = 3, 8, 16, 40
+    w, k, v, q, eta = _layer_inputs(rng, H, d, m, n, 20, scale=0.3)
+    w_hat, g, ns = oracle.update(*w, k, v, eta, 0.05, 1)
+    k2 = k.copy()
+    k2[:, d:] = rng.normal(0, 1, (n, (H - 1) * d))
+    w_hat2, _, _ = oracle.update(*w, k2, v, eta, 0.05, 1)
+    for j in range(3):
+        assert np.array_equal(w_hat[j][0], w_hat2[j][0])
+        assert not np.array_equal(w_hat[j][1], w_hat2[j][1])
+    h = 1
+    c = slice(h * d, (h + 1) * d)
+    wh, gh, nh = oracle.update_head(w[0][h], w[1][h], w[2][h], k[:, c], v[:, c], eta[h], 0.05, 1)
+    for j in range(3):
+        assert np.array_equal(w_hat[j][h], wh[j])
+
+
+def test_empty_token_set_gives_zero_gradient_and_unchanged_w(rng):
+    w, k, v, q, eta = _layer_inputs(rng, 1, 8, 16, 0, 4)
+    w_hat, g, ns = oracle.update(*w, k, v, eta, 0.01, 1)
+    for j in range(3):
+        assert np.all(g[j] == 0) and np.all(ns[j] == 0)
+        assert np.array_equal(w_hat[j], w[j])
+
+
+def test_query_only_rows_do_not_change_w(rng):
+    w, k, v, q, eta = _layer_inputs(rng, 1, 8, 16, 30, 50, scale=0.3)
+    w_hat, _, _ = oracle.update(*w, k, v, eta, 0.05, 1)
+    o_all = oracle.apply(*w_hat, q)
+    o_part = oracle.apply(*w_hat, q[:30])
+    assert np.array_equal(o_all[:30], o_part)
+
+
+# -------------------------------------------------------------------- streaming
+def test_stream_single_chunk_is_offline_update_after_apply(rng):
+    w, k, v, q, eta = _layer_inputs(rng, 2, 8, 16, 40, 40, scale=0.3)
+    o, wf = oracle.stream(*w, k, v, eta, q, 0.05, 1, chunk=40)
+    np.testing.assert_array_equal(o, oracle.apply(*w, q))
+    w_off, _, _ = oracle.update(*w, k, v, eta, 0.05, 1)
+    for a, b in zip(wf, w_off):
+        assert np.array_equal(a, b)
+
+
+def test_stream_equals_sequential_calls(rng):
+    w, k, v, q, eta = _layer_inputs(rng, 2, 8, 16, 70, 70, scale=0.3)
+    o, wf = oracle.stream(*w, k, v, eta, q, 0.05, 1, chunk=25)
+    cur = w
+    for t0 in (0, 25, 50):
+        t1 = min(70, t0 + 25)
+        np.testing.assert_array_equal(o[t0:t1], oracle.apply(*cur, q[t0:t1]))
+        cur, _, _ = oracle.update(*cur, k[t0:t1], v[t0:t1], eta[:, t0:t1], 0.05, 1)
+    for a, b in zip(wf, cur):
+        assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ ShortConv2D
+def test_shortconv2d_matches_library_depthwise_conv(rng):
+    frames, gh, gw, sp, C = 3, 5, 7, 2, 6
+    tpf = sp + gh * gw
+    v = rng.normal(0, 1, (frames * tpf, C))
+    wc = rng.normal(0, 0.1, (C, 3, 3))
+    out = oracle.shortconv2d(v, wc, frames, tpf, sp, gh, gw)
+    img = torch.from_numpy(v.reshape(frames, tpf, C)[:, sp:].reshape(frames, gh, gw, C)).permute(0, 3, 1, 2)
+    ref = torch.nn.functional.conv2d(img, torch.from_numpy(wc)[:, None], padding=1, groups=C)
+    ref = ref.permute(0, 2, 3, 1).reshape(frames, gh * gw, C).numpy()
+    got = out.reshape(frames, tpf, C)
+    np.testing.assert_allclose(got[:, sp:], ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(got[:, :sp], v.reshape(frames, tpf, C)[:, :sp])
+
+
+def test_shortconv2d_delta_and_box_closed_forms(rng):
+    C = 4
+    v = rng.normal(0, 1, (2 * 9, C))
+    delta = np.zeros((C, 3, 3))
+    delta[:, 1, 1] = 1.0
+    np.testing.assert_array_equal(oracle.shortconv2d(v, delta, 2, 9, 0, 3, 3), v)
+    ones = np.ones((1 * 9, 1))
+    box = oracle.shortconv2d(ones, np.ones((1, 3, 3)), 1, 9, 0, 3, 3).reshape(3, 3)
+    np.testing.assert_array_equal(box, np.array([[4, 6, 4], [6, 9, 6], [4, 6, 4]], float))
+    # an off-centre tap shifts the image: w[dy+1, dx+1] picks V[y+dy, x+dx]
+    shift = np.zeros((1, 3, 3))
+    shift[0, 2, 1] = 1.0                 # dy = +1: output row y reads input row y+1
+    img = np.arange(9, dtype=float).reshape(9, 1)
+    got = oracle.shortconv2d(img, shift, 1, 9, 0, 3, 3).reshape(3, 3)
+    np.testing.assert_array_equal(got, np.array([[3, 4, 5], [6, 7, 8], [0, 0, 0]], float))
+
+
+# ------------------------------------------------------- oracle's own rounding
+def test_fp32_oracle_within_1e5_of_fp64(rng):
+    H, d, m, n = 2, 64, 128, 3000
+    w, k, v, q, eta = _layer_inputs(rng, H, d, m, n, 500)
+    w32 = [x.astype(np.float32) for x in w]
+    o64, wh64, g64, ns64 = oracle.layer(*w, k, v, eta, q, 0.01, 1)
+    o32, wh32, g32, ns32 = oracle.layer(*w32, k.astype(np.float32), v.astype(np.float32),
+                                        eta.astype(np.float32), q.astype(np.float32), 0.01, 1)
+    assert o32.dtype == np.float32 and g32[0].dtype == np.float32
+    for a, b in zip(g32 + ns32 + wh32, g64 + ns64 + wh64):
+        for h in range(H):
+            assert rel_fro(a[h], b[h]) <= 1e-5
+    assert rel_fro(o32, o64) <= 1e-5
