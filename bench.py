@@ -1,0 +1,197 @@
+"""Throughput of the LaCT layer (ShortConv2D + update + apply) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5a]
+
+One step is one pass of the whole layer over the workload's synthetic tokens,
+already resident in HBM: V' = ShortConv2D(V) (if the workload has it), the
+update with the workload's inner steps, and apply over every query row.
+Prints one JSON line.  ``value`` is update tokens per second.  The ``roofline``
+entry covers the gradient kernel, timed with HIP events on its own stream
+inside the timed region.  ``cpu_baseline`` times the CPU oracle (fp32 NumPy)
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c5a")
+    ap.add_argument("--frames", type=int, default=0, help="override the workload's frame count")
+    ap.add_argument("--cpu-sample-frames", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--no-profile-events", action="store_true")
+    return ap.parse_args()
+
+
+def flops(cfg, n, nq):
+    """Algorithmic FLOPs: update 12*N*d*m*H per inner step, apply 6*Nq*d*m*H."""
+    H, d, m = cfg.heads, cfg.d, cfg.m
+    grad = 12.0 * n * d * m * H
+    apply = 6.0 * nq * d * m * H
+    r, c = min(d, m), max(d, m)
+    ns = 5 * (4.0 * r * r * c + 2.0 * r ** 3) * 3 * H
+    conv = 18.0 * n * H * d if cfg.conv else 0.0
+    return grad, apply, ns, conv
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30   # 1 GiB
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def cpu_baseline(cfg, frames):
+    """Time the fp32 NumPy oracle on `frames` frames of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from test_weight_layers_amd import synth
+    n = frames * cfg.tokens_per_frame
+    inp = synth.make_inputs(cfg, n=n, nq_extra=0)
+    f32 = lambda t: t.detach().float().numpy()
+    args = [f32(inp.w1), f32(inp.w3), f32(inp.w2), f32(inp.k), f32(inp.v), f32(inp.eta), f32(inp.q)]
+    conv = None
+    if cfg.conv:
+        conv = dict(wconv=f32(inp.wconv), frames=frames, tokens_per_frame=cfg.tokens_per_frame,
+                    n_special=cfg.n_special, grid_h=cfg.grid_h, grid_w=cfg.grid_w)
+    t0 = time.perf_counter()
+    oracle.layer(*args, cfg.lr, cfg.steps, conv=conv)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{frames} frames x {cfg.tokens_per_frame} tokens = {n} tokens of {cfg.name}, "
+                      f"fp32 NumPy oracle, full layer (conv={cfg.conv}, steps={cfg.steps}, apply), "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding "
+              "is a design note, not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from test_weight_layers_amd import synth, ttt
+    from test_weight_layers_amd.configs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    if args.frames:
+        cfg = cfg.with_frames(args.frames)
+    if cfg.chunk_frames:
+        raise SystemExit("streaming workloads are timed by bench_stream (not in this script)")
+    torch.cuda.set_device(0)
+    ttt.load()
+    t_gen = time.perf_counter()
+    inp = synth.to_device(synth.make_inputs(cfg), "cuda")
+    gen_s = time.perf_counter() - t_gen
+    H, d, m = cfg.heads, cfg.d, cfg.m
+    n, nq = inp.k.shape[0], inp.q.shape[0]
+    dt = inp.k.dtype
+    geo = dict(frames=cfg.frames, tokens_per_frame=cfg.tokens_per_frame, n_special=cfg.n_special,
+               grid_h=cfg.grid_h, grid_w=cfg.grid_w)
+    w0 = (inp.w1, inp.w3, inp.w2)
+    w_out = tuple(torch.empty_like(x) for x in w0)
+    v2 = torch.empty_like(inp.v)
+    o = torch.empty((nq, H * d), dtype=dt, device="cuda")
+    ws_u = torch.empty(ttt.update_workspace_bytes(H, d, m, n, dt), dtype=torch.uint8, device="cuda")
+    nws = ttt.apply_workspace_bytes(H, d, m, nq, dt)
+    ws_a = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+
+    def step():
+        v = inp.v
+        if cfg.conv:
+            ttt.shortconv2d(inp.v, inp.wconv, **geo, out=v2)
+            v = v2
+        ttt.update(w0, inp.k, v, inp.eta, cfg.lr, cfg.steps, out=w_out, workspace=ws_u)
+        ttt.apply(w_out, inp.q, out=o, workspace=ws_a)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    prof = not args.no_profile_events
+    ttt.profile_reset()
+    ttt.profile_enable(prof)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ttt.profile_enable(False)
+    kt = ttt.profile_read() if prof else {}
+    ms_step = elapsed * 1e3 / args.steps
+
+    grad_f, apply_f, ns_f, conv_f = flops(cfg, n, nq)
+    value = n * args.steps / elapsed
+    out = {
+        "metric": "TTT layer tokens/sec (update+apply) on 1 MI355X; % dense-bf16 MFMA peak",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32", "data": "synthetic (seeded N(0,1)/U(0,0.1) tokens, "
+        "random-init fast weights)",
+        "config": {"workload": cfg.name, "frames": cfg.frames, "tokens_per_frame": cfg.tokens_per_frame,
+                   "update_tokens": n, "apply_tokens": nq, "heads": H, "d": d, "hidden": m,
+                   "inner_steps": cfg.steps, "shortconv2d": cfg.conv, "lr": cfg.lr},
+        "input_gen_s": round(gen_s, 2),
+    }
+    peak = PEAK_BF16_TFLOPS if dt == torch.bfloat16 else PEAK_F32_TFLOPS
+    if kt:
+        g_ms, g_n = kt["grad"]
+        a_ms, a_n = kt["apply"]
+        per_kernel = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
+                      for k, v in kt.items()}
+        out["kernels"] = per_kernel
+        gemm_flops = (grad_f * cfg.steps + apply_f) * args.steps
+        out["mfma_pct_gemm_phases"] = 100.0 * gemm_flops / ((g_ms + a_ms) * 1e-3) / (peak * 1e12)
+        out["mfma_pct_whole_layer"] = 100.0 * (gemm_flops + ns_f * cfg.steps * args.steps) / elapsed / (peak * 1e12)
+        grad_avg_s = g_ms * 1e-3 / g_n
+        achieved = grad_f / grad_avg_s / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "grad (fused forward + SwiGLU backward + weight-gradient "
+                           "contractions)", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                           "frac": achieved / peak, "traffic": None,
+                           "avg_launch_ms": grad_avg_s * 1e3, "flop_per_launch": grad_f}
+        if a_n:
+            a_avg = a_ms * 1e-3 / a_n
+            out["apply_kernel"] = {"achieved_tflops": apply_f / a_avg / 1e12, "frac": apply_f / a_avg / 1e12 / peak,
+                                   "avg_launch_ms": a_avg * 1e3}
+        if cfg.conv and kt["conv"][1]:
+            c_avg = kt["conv"][0] * 1e-3 / kt["conv"][1]
+            conv_bytes = 2.0 * n * H * d * inp.v.element_size()
+            out["conv_kernel"] = {"achieved_gbs": conv_bytes / c_avg / 1e9, "peak_gbs": PEAK_HBM_GBS,
+                                  "frac": conv_bytes / c_avg / 1e9 / PEAK_HBM_GBS, "avg_launch_ms": c_avg * 1e3}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample_frames, cfg.frames))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,463 @@
+// C ABI of libttt.so (declared in include/ttt.h): argument checks, workspace
+// planning and the launch sequences of the LaCT layer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/ttt.h"
+#include "kernels.h"
+
+using namespace ttt;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+// ----------------------------------------------------------------- options
+int64_t g_force_general = 0;   // 1: use the general kernels even where a fast one exists
+int64_t g_splits = 0;          // >0: fixed number of token splits for the gradient
+
+// ----------------------------------------------------------------- timing
+struct Pending {
+  int kind;
+  hipEvent_t e0, e1;
+};
+std::mutex g_prof_mu;
+bool g_prof = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_free_events;
+double g_ms[TTT_K_COUNT];
+int64_t g_count[TTT_K_COUNT];
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+int run(int kind, const char *what, hipStream_t s, F &&f) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_prof) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    e0 = take_event();
+    e1 = take_event();
+    if (e0) hipEventRecord(e0, s);
+  }
+  const hipError_t err = f();
+  if (g_prof && e0 && e1) {
+    hipEventRecord(e1, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_pending.push_back({kind, e0, e1});
+  }
+  if (err != hipSuccess) return fail(TTT_EHIP, "%s: %s", what, hipGetErrorString(err));
+  return TTT_OK;
+}
+
+// ----------------------------------------------------------------- checks
+bool d_supported(int d) { return d == 64 || d == 128 || d == 256 || d == 512 || d == 768 || d == 1024; }
+
+int check_shape(int heads, int d, int m, int dtype) {
+  if (heads < 1) return fail(TTT_EINVAL, "heads must be >= 1 (got %d)", heads);
+  if (dtype != TTT_F32 && dtype != TTT_BF16) return fail(TTT_EUNSUPPORTED, "unknown dtype %d", dtype);
+  if (!d_supported(d)) return fail(TTT_EUNSUPPORTED, "d=%d not in {64,128,256,512,768,1024}", d);
+  if (m < 64 || m % 64 != 0) return fail(TTT_EUNSUPPORTED, "m=%d must be a positive multiple of 64", m);
+  return TTT_OK;
+}
+
+size_t esize(int dtype) { return dtype == TTT_BF16 ? 2 : 4; }
+
+int check_rows(const void *p, int64_t ld, int heads, int d, int dtype, const char *name) {
+  if (!p) return fail(TTT_EINVAL, "%s is null", name);
+  if (ld < (int64_t)heads * d) return fail(TTT_EINVAL, "ld of %s (%lld) < heads*d (%d)", name, (long long)ld, heads * d);
+  if (((uintptr_t)p) % 16 != 0 || (ld * (int64_t)esize(dtype)) % 16 != 0)
+    return fail(TTT_EINVAL, "%s rows must be 16-byte aligned", name);
+  return TTT_OK;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ----------------------------------------------------------------- update plan
+struct UpdatePlan {
+  int H, d, m, r, c;
+  bool bf16, fast, xcd;
+  int dchunks, splits, grid;
+  int64_t n, nblk;
+  size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_a, off_b, total;
+};
+
+UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
+  UpdatePlan p{};
+  p.H = H, p.d = d, p.m = m, p.n = n;
+  p.r = d < m ? d : m;
+  p.c = d < m ? m : d;
+  p.bf16 = dtype == TTT_BF16;
+  p.fast = !g_force_general && grad_fast_supported(d, p.bf16);
+  p.dchunks = p.fast ? 1 : d / grad_general_dc(d, p.bf16);
+  p.nblk = (n + kTokBlock - 1) / kTokBlock;
+  const int mtiles = m / kHidTile;
+  const int64_t per_split = (int64_t)H * mtiles * p.dchunks;
+  const int64_t target = p.fast ? 256 : 1024;     // one fast workgroup fills a CU
+  int64_t s = (target + per_split - 1) / per_split;
+  if (g_splits > 0) s = g_splits;
+  if (p.nblk > 0 && s > p.nblk) s = p.nblk;
+  if (s < 1) s = 1;
+  p.splits = (int)s;
+  p.grid = (int)(per_split * s);
+  p.xcd = p.fast && p.grid % 8 == 0 && (p.grid / 8) % mtiles == 0;
+  const size_t mat = (size_t)H * d * m;
+  size_t off = 0;
+  p.off_wop = off;
+  off = align256(off + (p.bf16 ? 3 * mat * 2 : mat * 4));
+  p.off_part = off;
+  off = align256(off + (size_t)p.splits * 3 * mat * 4);
+  p.off_g = off;
+  off = align256(off + 3 * mat * 4);
+  p.off_sumsq = off;
+  off = align256(off + 3 * mat / 4096 * 4);
+  p.off_x0 = off;
+  off = align256(off + 3 * mat * 4);
+  p.off_x1 = off;
+  off = align256(off + 3 * mat * 4);
+  p.off_a = off;
+  off = align256(off + (size_t)3 * H * p.r * p.r * 4);
+  p.off_b = off;
+  off = align256(off + (size_t)3 * H * p.r * p.r * 4);
+  p.total = off;
+  return p;
+}
+
+size_t apply_ws(int H, int d, int m, int dtype) {
+  return dtype == TTT_BF16 ? align256((size_t)3 * H * d * m * 2) : 0;
+}
+
+struct W3 {
+  const float *w1, *w3, *w2;
+};
+struct W3o {
+  float *w1, *w3, *w2;
+};
+
+// Muon's quintic Newton-Schulz coefficients and the Frobenius-norm guard.
+constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
+constexpr int kNsIters = 5;
+constexpr float kNsEps = 1e-7f;
+
+int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v, int64_t ld, const float *eta,
+              int64_t eta_hs, float lr, int steps, float *grad_out, float *ns_out, char *ws, hipStream_t s) {
+  const size_t mat = (size_t)P.H * P.d * P.m;
+  void *wop = ws + P.off_wop;
+  float *part = reinterpret_cast<float *>(ws + P.off_part);
+  float *g = reinterpret_cast<float *>(ws + P.off_g);
+  float *sumsq = reinterpret_cast<float *>(ws + P.off_sumsq);
+  float *x0 = reinterpret_cast<float *>(ws + P.off_x0);
+  float *x1 = reinterpret_cast<float *>(ws + P.off_x1);
+  float *am = reinterpret_cast<float *>(ws + P.off_a);
+  float *bm = reinterpret_cast<float *>(ws + P.off_b);
+  const NsShape sh{P.H, P.d, P.m};
+  int st;
+  for (int t = 0; t < steps; ++t) {
+    const W3 src = t == 0 ? in : W3{out.w1, out.w3, out.w2};
+    const bool last = t == steps - 1;
+    GradParams gp{};
+    gp.k = k, gp.v = v, gp.ld = ld, gp.eta = eta, gp.eta_hs = eta_hs;
+    if (P.bf16) {
+      __bf16 *b = static_cast<__bf16 *>(wop);
+      st = run(TTT_K_CAST, "cast", s, [&] {
+        return launch_cast(src.w1, src.w3, src.w2, b, b + mat, b + 2 * mat, nullptr, P.H, P.d, P.m, true, s);
+      });
+      if (st) return st;
+      gp.w1 = b, gp.w3 = b + mat, gp.w2t = b + 2 * mat;
+    } else {
+      float *w2t = static_cast<float *>(wop);
+      st = run(TTT_K_CAST, "cast", s, [&] {
+        return launch_cast(src.w1, src.w3, src.w2, nullptr, nullptr, w2t, nullptr, P.H, P.d, P.m, false, s);
+      });
+      if (st) return st;
+      gp.w1 = src.w1, gp.w3 = src.w3, gp.w2t = w2t;
+    }
+    gp.part = part, gp.n = P.n, gp.nblk = P.nblk;
+    gp.heads = P.H, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
+    st = run(TTT_K_GRAD, "gradient", s, [&] { return launch_grad(gp, P.d, P.bf16, P.fast, P.grid, s); });
+    if (st) return st;
+    st = run(TTT_K_REDUCE, "reduce", s, [&] {
+      return launch_reduce(part, P.splits, (int64_t)3 * mat, g, last ? grad_out : nullptr, sumsq, s);
+    });
+    if (st) return st;
+    st = run(TTT_K_NS, "ns_normalize", s, [&] { return launch_ns_normalize(g, sumsq, x0, sh, kNsEps, s); });
+    if (st) return st;
+    float *x = x0, *xn = x1;
+    const int B = 3 * P.H;
+    const int64_t srr = (int64_t)P.r * P.r, src_ = (int64_t)P.r * P.c;
+    for (int it = 0; it < kNsIters; ++it) {
+      GemmBatch g1{x, x, nullptr, am, P.r, P.r, P.c, P.c, P.c, 0, P.r, 1, src_, src_, 0, srr, 1.0f, 0.0f, B};
+      GemmBatch g2{am, am, am, bm, P.r, P.r, P.r, P.r, P.r, P.r, P.r, 1, srr, srr, srr, srr, kNsC, kNsB, B};
+      GemmBatch g3{bm, x, x, xn, P.r, P.c, P.r, P.r, P.c, P.c, P.c, 0, srr, src_, src_, src_, 1.0f, kNsA, B};
+      st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g1, s); });
+      if (st) return st;
+      st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g2, s); });
+      if (st) return st;
+      st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g3, s); });
+      if (st) return st;
+      float *tmp = x;
+      x = xn;
+      xn = tmp;
+    }
+    st = run(TTT_K_NS, "ns_step", s, [&] {
+      return launch_ns_step(x, src.w1, src.w3, src.w2, out.w1, out.w3, out.w2, last ? ns_out : nullptr, lr, sh, s);
+    });
+    if (st) return st;
+  }
+  return TTT_OK;
+}
+
+int do_apply(int H, int d, int m, W3 w, const void *q, int64_t ldq, void *o, int64_t ldo, int64_t nq, int dtype,
+             char *ws, hipStream_t s) {
+  if (nq == 0) return TTT_OK;
+  const bool bf16 = dtype == TTT_BF16;
+  const bool fast = !g_force_general && apply_fast_supported(d, bf16);
+  ApplyParams ap{};
+  ap.q = q, ap.ldq = ldq, ap.o = o, ap.ldo = ldo, ap.nq = nq, ap.heads = H, ap.m = m;
+  ap.dchunks = fast ? 1 : d / apply_general_dc(d, bf16);
+  if (bf16) {
+    const size_t mat = (size_t)H * d * m;
+    __bf16 *b = reinterpret_cast<__bf16 *>(ws);
+    const int st = run(TTT_K_CAST, "cast", s, [&] {
+      return launch_cast(w.w1, w.w3, w.w2, b, b + mat, nullptr, b + 2 * mat, H, d, m, true, s);
+    });
+    if (st) return st;
+    ap.w1 = b, ap.w3 = b + mat, ap.w2 = b + 2 * mat;
+  } else {
+    ap.w1 = w.w1, ap.w3 = w.w3, ap.w2 = w.w2;
+  }
+  return run(TTT_K_APPLY, "apply", s, [&] { return launch_apply(ap, d, bf16, fast, s); });
+}
+
+int check_ws(void *ws, size_t have, size_t need) {
+  if (need == 0) return TTT_OK;
+  if (!ws) return fail(TTT_EWORKSPACE, "workspace is null (need %zu bytes)", need);
+  if (((uintptr_t)ws) % 256 != 0) return fail(TTT_EINVAL, "workspace must be 256-byte aligned");
+  if (have < need) return fail(TTT_EWORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  return TTT_OK;
+}
+
+int check_weights(const float *w1, const float *w3, const float *w2) {
+  if (!w1 || !w3 || !w2) return fail(TTT_EINVAL, "fast-weight pointer is null");
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ttt_last_error(void) { return g_err.c_str(); }
+
+int ttt_update_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t n, int32_t dtype, size_t *bytes) {
+  int st = check_shape(heads, d, m, dtype);
+  if (st) return st;
+  if (n < 0) return fail(TTT_EINVAL, "n must be >= 0");
+  if (!bytes) return fail(TTT_EINVAL, "bytes is null");
+  *bytes = plan_update(heads, d, m, n, dtype).total;
+  return TTT_OK;
+}
+
+int ttt_apply_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t nq, int32_t dtype, size_t *bytes) {
+  int st = check_shape(heads, d, m, dtype);
+  if (st) return st;
+  if (nq < 0) return fail(TTT_EINVAL, "nq must be >= 0");
+  if (!bytes) return fail(TTT_EINVAL, "bytes is null");
+  *bytes = apply_ws(heads, d, m, dtype);
+  return TTT_OK;
+}
+
+int ttt_stream_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t chunk, int32_t dtype, size_t *bytes) {
+  int st = check_shape(heads, d, m, dtype);
+  if (st) return st;
+  if (chunk < 1) return fail(TTT_EINVAL, "chunk must be >= 1");
+  if (!bytes) return fail(TTT_EINVAL, "bytes is null");
+  const size_t a = plan_update(heads, d, m, chunk, dtype).total, b = apply_ws(heads, d, m, dtype);
+  *bytes = a > b ? a : b;
+  return TTT_OK;
+}
+
+int ttt_update(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2, float *w1_out,
+               float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv, const float *eta,
+               int64_t eta_head_stride, int64_t n, float lr, int32_t steps, int32_t dtype, float *grad_out,
+               float *ns_out, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape(heads, d, m, dtype);
+  if (st) return st;
+  if ((st = check_weights(w1, w3, w2))) return st;
+  if (!w1_out || !w3_out || !w2_out) return fail(TTT_EINVAL, "output fast-weight pointer is null");
+  const size_t wb = (size_t)heads * d * m * 4;
+  const float *ins[3] = {w1, w3, w2};
+  float *outs[3] = {w1_out, w3_out, w2_out};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (overlap(ins[i], wb, outs[j], wb) && !(i == j && ins[i] == outs[j]))
+        return fail(TTT_EINVAL, "output weights must equal their input or not overlap any input");
+  if (n < 0) return fail(TTT_EINVAL, "n must be >= 0");
+  if (steps < 1) return fail(TTT_EINVAL, "steps must be >= 1");
+  if (!std::isfinite(lr)) return fail(TTT_EINVAL, "lr must be finite");
+  if (n > 0) {
+    if ((st = check_rows(k, ld_kv, heads, d, dtype, "k"))) return st;
+    if ((st = check_rows(v, ld_kv, heads, d, dtype, "v"))) return st;
+    if (!eta) return fail(TTT_EINVAL, "eta is null");
+    if (eta_head_stride < 0) return fail(TTT_EINVAL, "eta_head_stride must be >= 0");
+  }
+  const UpdatePlan P = plan_update(heads, d, m, n, dtype);
+  if ((st = check_ws(workspace, workspace_bytes, P.total))) return st;
+  return do_update(P, W3{w1, w3, w2}, W3o{w1_out, w3_out, w2_out}, k, v, ld_kv, eta, eta_head_stride, lr, steps,
+                   grad_out, ns_out, static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int ttt_apply(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2, const void *q,
+              int64_t ld_q, void *o, int64_t ld_o, int64_t nq, int32_t dtype, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  int st = check_shape(heads, d, m, dtype);
+  if (st) return st;
+  if ((st = check_weights(w1, w3, w2))) return st;
+  if (nq < 0) return fail(TTT_EINVAL, "nq must be >= 0");
+  if (nq > 0) {
+    if ((st = check_rows(q, ld_q, heads, d, dtype, "q"))) return st;
+    if ((st = check_rows(o, ld_o, heads, d, dtype, "o"))) return st;
+    if (overlap(q, (size_t)nq * ld_q * esize(dtype), o, (size_t)nq * ld_o * esize(dtype)))
+      return fail(TTT_EINVAL, "q and o must not overlap");
+  }
+  if ((st = check_ws(workspace, workspace_bytes, apply_ws(heads, d, m, dtype)))) return st;
+  return do_apply(heads, d, m, W3{w1, w3, w2}, q, ld_q, o, ld_o, nq, dtype, static_cast<char *>(workspace),
+                  static_cast<hipStream_t>(stream));
+}
+
+int ttt_shortconv2d(const void *v, void *v_out, int64_t ld, const float *wconv, int32_t frames,
+                    int32_t tokens_per_frame, int32_t n_special, int32_t grid_h, int32_t grid_w, int32_t channels,
+                    int32_t dtype, void *stream) {
+  if (dtype != TTT_F32 && dtype != TTT_BF16) return fail(TTT_EUNSUPPORTED, "unknown dtype %d", dtype);
+  if (frames < 0 || n_special < 0 || grid_h < 1 || grid_w < 1 || channels < 8)
+    return fail(TTT_EINVAL, "bad conv geometry");
+  if (tokens_per_frame != n_special + grid_h * grid_w)
+    return fail(TTT_EINVAL, "tokens_per_frame (%d) != n_special + grid_h*grid_w (%d)", tokens_per_frame,
+                n_special + grid_h * grid_w);
+  if (channels % 8 != 0) return fail(TTT_EUNSUPPORTED, "channels must be a multiple of 8");
+  if (frames == 0) return TTT_OK;
+  if (!wconv) return fail(TTT_EINVAL, "wconv is null");
+  int st;
+  if ((st = check_rows(v, ld, 1, channels, dtype, "v"))) return st;
+  if ((st = check_rows(v_out, ld, 1, channels, dtype, "v_out"))) return st;
+  const size_t bytes = (size_t)frames * tokens_per_frame * ld * esize(dtype);
+  if (overlap(v, bytes, v_out, bytes)) return fail(TTT_EINVAL, "v and v_out must not overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run(TTT_K_CONV, "shortconv2d", s, [&] {
+    return launch_conv(v, v_out, ld, wconv, frames, tokens_per_frame, n_special, grid_h, grid_w, channels,
+                       dtype == TTT_BF16, s);
+  });
+}
+
+int ttt_stream(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float *w2, const void *k, const void *v,
+               int64_t ld_kv, const float *eta, int64_t eta_head_stride, const void *q, int64_t ld_q, void *o,
+               int64_t ld_o, int64_t n, int64_t chunk, float lr, int32_t steps, int32_t dtype, void *workspace,
+               size_t workspace_bytes, void *stream) {
+  int st = check_shape(heads, d, m, dtype);
+  if (st) return st;
+  if ((st = check_weights(w1, w3, w2))) return st;
+  if (n < 0 || chunk < 1 || steps < 1) return fail(TTT_EINVAL, "need n >= 0, chunk >= 1, steps >= 1");
+  if (!std::isfinite(lr)) return fail(TTT_EINVAL, "lr must be finite");
+  if (n == 0) return TTT_OK;
+  if ((st = check_rows(k, ld_kv, heads, d, dtype, "k"))) return st;
+  if ((st = check_rows(v, ld_kv, heads, d, dtype, "v"))) return st;
+  if ((st = check_rows(q, ld_q, heads, d, dtype, "q"))) return st;
+  if ((st = check_rows(o, ld_o, heads, d, dtype, "o"))) return st;
+  if (!eta || eta_head_stride < 0) return fail(TTT_EINVAL, "eta is null or has a negative head stride");
+  size_t need = 0;
+  ttt_stream_workspace_bytes(heads, d, m, chunk, dtype, &need);
+  if ((st = check_ws(workspace, workspace_bytes, need))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  const size_t es = esize(dtype);
+  for (int64_t t0 = 0; t0 < n; t0 += chunk) {
+    const int64_t len = n - t0 < chunk ? n - t0 : chunk;
+    st = do_apply(heads, d, m, W3{w1, w3, w2}, static_cast<const char *>(q) + t0 * ld_q * es, ld_q,
+                  static_cast<char *>(o) + t0 * ld_o * es, ld_o, len, dtype, ws, s);
+    if (st) return st;
+    const UpdatePlan P = plan_update(heads, d, m, len, dtype);
+    st = do_update(P, W3{w1, w3, w2}, W3o{w1, w3, w2}, static_cast<const char *>(k) + t0 * ld_kv * es,
+                   static_cast<const char *>(v) + t0 * ld_kv * es, ld_kv, eta + t0, eta_head_stride, lr, steps,
+                   nullptr, nullptr, ws, s);
+    if (st) return st;
+  }
+  return TTT_OK;
+}
+
+int ttt_set_option(int32_t option, int64_t value) {
+  switch (option) {
+    case TTT_OPT_FORCE_GENERAL: g_force_general = value != 0; return TTT_OK;
+    case TTT_OPT_SPLITS:
+      if (value < 0) return fail(TTT_EINVAL, "splits must be >= 0");
+      g_splits = value;
+      return TTT_OK;
+  }
+  return fail(TTT_EINVAL, "unknown option %d", option);
+}
+
+int ttt_profile_enable(int32_t on) {
+  g_prof = on != 0;
+  return TTT_OK;
+}
+
+int ttt_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto &p : g_pending) {
+    hipEventSynchronize(p.e1);
+    g_free_events.push_back(p.e0);
+    g_free_events.push_back(p.e1);
+  }
+  g_pending.clear();
+  for (int i = 0; i < TTT_K_COUNT; ++i) g_ms[i] = 0.0, g_count[i] = 0;
+  return TTT_OK;
+}
+
+int ttt_profile_read(int32_t kind, double *total_ms, int64_t *launches) {
+  if (kind < 0 || kind >= TTT_K_COUNT || !total_ms || !launches) return fail(TTT_EINVAL, "bad profile query");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto &p : g_pending) {
+    hipError_t e = hipEventSynchronize(p.e1);
+    if (e != hipSuccess) return fail(TTT_EHIP, "profile: %s", hipGetErrorString(e));
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, p.e0, p.e1);
+    if (e != hipSuccess) return fail(TTT_EHIP, "profile: %s", hipGetErrorString(e));
+    g_ms[p.kind] += ms;
+    g_count[p.kind] += 1;
+    g_free_events.push_back(p.e0);
+    g_free_events.push_back(p.e1);
+  }
+  g_pending.clear();
+  *total_ms = g_ms[kind];
+  *launches = g_count[kind];
+  return TTT_OK;
+}
+
+}  // extern "C"

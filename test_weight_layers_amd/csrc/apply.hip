@@ -1,0 +1,242 @@
+// Apply: o = f_W(q) = W2 (SiLU(W1 q) o (W3 q)) for every query row
+// (Scal3R eq. (4); ZipMap 关键设计 1; tttLRM query-only tokens use the same pass).
+//
+// Two back-to-back contractions per head: Z = W1 Q^T, W3 Q^T over d (computed
+// transposed, hidden units as MFMA rows), the SiLU-gate in registers, then
+// O^T += W2 H^T over the hidden units.  The hidden rows of each 32-unit chunk
+// are permuted (perm_row) so that the accumulator layout of the first product
+// is the operand layout of the second; H never leaves registers.
+#include "common.h"
+#include "kernels.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kHidChunk = 32;
+
+// ---------------------------------------------------------------- fast path
+// bf16, D <= 256.  A workgroup owns 128 tokens of one head (32 per wave) and
+// streams the head's weights through LDS 32 hidden units at a time; each wave
+// keeps its Q fragments and its O^T accumulators in registers.
+template <int D>
+struct ApplyLayout {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kW13 = kHidChunk * kRowBytes;   // one W1 / W3 chunk [32][D]
+  static constexpr int kW2 = D * kHidChunk * 2;         // W2 chunk [D][32]
+  static constexpr int kBytes = 2 * kW13 + kW2;
+  static __device__ __forceinline__ int w13(int mat, int r, int c) {
+    return mat * kW13 + r * kRowBytes + 16 * (c ^ swz_rows(r));
+  }
+  static __device__ __forceinline__ int w2(int rho, int a) { return 2 * kW13 + rho * 64 + 16 * (a ^ swz_64(rho)); }
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
+  using L = ApplyLayout<D>;
+  constexpr int KC = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
+
+  const int h = blockIdx.x % p.heads;
+  const int64_t tile = blockIdx.x / p.heads;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int64_t tok0 = tile * 128 + 32 * w;
+
+  // Q^T fragments (B operand): token tok0 + 16t + li, d = 32 kc + 8g .. +8
+  bf16x8 qf[2][KC];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int64_t tok = tok0 + 16 * t + li;
+    const __bf16 *Q = static_cast<const __bf16 *>(p.q) + tok * p.ldq + (int64_t)h * D + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qf[t][kc] = (tok < p.nq) ? ld8(Q + 32 * kc) : zero8<__bf16>();
+  }
+  f32x4 acc[DT][2];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc[i][0] = acc[i][1] = f32x4{0, 0, 0, 0};
+
+  const __bf16 *W1 = static_cast<const __bf16 *>(p.w1) + (int64_t)h * p.m * D;
+  const __bf16 *W3 = static_cast<const __bf16 *>(p.w3) + (int64_t)h * p.m * D;
+  const __bf16 *W2 = static_cast<const __bf16 *>(p.w2) + (int64_t)h * D * p.m;
+
+  for (int hc = 0; hc < p.m / kHidChunk; ++hc) {
+    __syncthreads();
+    // stage W1, W3 rows [32 hc, 32 hc + 32) and W2 columns of the same units
+    for (int e = tid; e < 2 * kHidChunk * (D / 8); e += 256) {
+      const int mat = e / (kHidChunk * (D / 8));
+      const int rem = e % (kHidChunk * (D / 8));
+      const int r = rem / (D / 8), c = rem % (D / 8);
+      const __bf16 *src = (mat ? W3 : W1) + (int64_t)(hc * kHidChunk + r) * D + 8 * c;
+      *reinterpret_cast<u32x4 *>(smem + L::w13(mat, r, c)) = *reinterpret_cast<const u32x4 *>(src);
+    }
+    for (int e = tid; e < D * 4; e += 256) {
+      const int rho = e >> 2, a = e & 3;
+      const __bf16 *src = W2 + (int64_t)rho * p.m + hc * kHidChunk + 8 * a;
+      *reinterpret_cast<u32x4 *>(smem + L::w2(rho, a)) = *reinterpret_cast<const u32x4 *>(src);
+    }
+    __syncthreads();
+
+    // Z^T rows = hidden perm_row(u, li) of the chunk, cols = tokens
+    f32x4 z1[2][2], z3[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) z1[u][t] = z3[u][t] = f32x4{0, 0, 0, 0};
+      const int rw = perm_row(u, li);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(smem + L::w13(0, rw, 4 * kc + g));
+        const bf16x8 a3 = *reinterpret_cast<const bf16x8 *>(smem + L::w13(1, rw, 4 * kc + g));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          z1[u][t] = mma(a1, qf[t][kc], z1[u][t]);
+          z3[u][t] = mma(a3, qf[t][kc], z3[u][t]);
+        }
+      }
+    }
+    // H = SiLU(z1) o z3; element v = 4u + r is hidden 8g + v of the chunk
+    bf16x8 hf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float hv[8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float z = z1[u][t][r];
+          hv[4 * u + r] = z * sigmoid_fast(z) * z3[u][t][r];
+        }
+      hf[t] = pack8<__bf16>(hv);
+    }
+    // O^T[d][tok] += W2[d][chunk] H^T
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 w2f = *reinterpret_cast<const bf16x8 *>(smem + L::w2(16 * dt + li, g));
+      acc[dt][0] = mma(w2f, hf[0], acc[dt][0]);
+      acc[dt][1] = mma(w2f, hf[1], acc[dt][1]);
+    }
+  }
+
+  // O[tok][16 dt + 4g + r] for r = 0..3: one 8-byte store per (dt, t)
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int64_t tok = tok0 + 16 * t + li;
+    if (tok >= p.nq) continue;
+    __bf16 *O = static_cast<__bf16 *>(p.o) + tok * p.ldo + (int64_t)h * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      bf16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[dt][t][r];
+      *reinterpret_cast<bf16x4 *>(O + 16 * dt) = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------- general path
+// Any supported d, fp32 or bf16: 16 tokens per wave, 64 per workgroup, one
+// output d-chunk of DC columns per workgroup; operands read from global
+// memory (L1/L2 resident).  The first contraction is recomputed per d-chunk.
+template <typename T, int D, int DC>
+__global__ __launch_bounds__(256) void apply_general_kernel(ApplyParams p) {
+  using F = typename FragOf<T>::type;
+  constexpr int KC = D / 32, DT = DC / 16;
+  const int h = blockIdx.x % p.heads;
+  int64_t rest = blockIdx.x / p.heads;
+  const int dc = rest % p.dchunks;
+  const int64_t tile = rest / p.dchunks;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int64_t tok = tile * 64 + 16 * w + li;
+  const bool ok = tok < p.nq;
+  const int d0 = dc * DC;
+
+  const T *Q = static_cast<const T *>(p.q) + (ok ? tok : 0) * p.ldq + (int64_t)h * D + 8 * g;
+  const T *W1 = static_cast<const T *>(p.w1) + (int64_t)h * p.m * D;
+  const T *W3 = static_cast<const T *>(p.w3) + (int64_t)h * p.m * D;
+  const T *W2 = static_cast<const T *>(p.w2) + (int64_t)h * D * p.m;
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc[i] = f32x4{0, 0, 0, 0};
+
+  for (int hc = 0; hc < p.m / kHidChunk; ++hc) {
+    f32x4 z1[2], z3[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      z1[u] = z3[u] = f32x4{0, 0, 0, 0};
+      const int64_t row = (int64_t)(hc * kHidChunk + perm_row(u, li)) * D + 8 * g;
+#pragma unroll 2
+      for (int kc = 0; kc < KC; ++kc) {
+        const F qf = ok ? ld8(Q + 32 * kc) : zero8<T>();
+        z1[u] = mma(ld8(W1 + row + 32 * kc), qf, z1[u]);
+        z3[u] = mma(ld8(W3 + row + 32 * kc), qf, z3[u]);
+      }
+    }
+    float hv[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float z = z1[u][r];
+        hv[4 * u + r] = z * sigmoid_fast(z) * z3[u][r];
+      }
+    const F hf = pack8<T>(hv);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const F w2f = ld8(W2 + (int64_t)(d0 + 16 * dt + li) * p.m + hc * kHidChunk + 8 * g);
+      acc[dt] = mma(w2f, hf, acc[dt]);
+    }
+  }
+  if (!ok) return;
+  T *O = static_cast<T *>(p.o) + tok * p.ldo + (int64_t)h * D + d0 + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) O[16 * dt + r] = from_f32<T>(acc[dt][r]);
+}
+
+template <typename T, int D>
+hipError_t launch_general(const ApplyParams &p, hipStream_t s) {
+  constexpr int DC = (D < 128) ? D : 128;
+  const int64_t tiles = (p.nq + 63) / 64;
+  const int64_t grid = tiles * p.heads * p.dchunks;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((apply_general_kernel<T, D, DC>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_general_d(const ApplyParams &p, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_general<T, 64>(p, s);
+    case 128: return launch_general<T, 128>(p, s);
+    case 256: return launch_general<T, 256>(p, s);
+    case 512: return launch_general<T, 512>(p, s);
+    case 768: return launch_general<T, 768>(p, s);
+    case 1024: return launch_general<T, 1024>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool apply_fast_supported(int d, bool bf16) { return bf16 && (d == 64 || d == 128 || d == 256); }
+int apply_general_dc(int d, bool) { return d < 128 ? d : 128; }
+
+hipError_t launch_apply(const ApplyParams &p, int d, bool bf16, bool fast, hipStream_t s) {
+  if (fast) {
+    const int64_t grid = (p.nq + 127) / 128 * p.heads;
+    if (grid == 0) return hipSuccess;
+    switch (d) {
+      case 64: hipLaunchKernelGGL(apply_fast_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+      case 128: hipLaunchKernelGGL(apply_fast_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+      case 256: hipLaunchKernelGGL(apply_fast_kernel<256>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  return bf16 ? launch_general_d<__bf16>(p, d, s) : launch_general_d<float>(p, d, s);
+}
+
+}  // namespace ttt

@@ -1,0 +1,351 @@
+// Fast-weight gradient of the eta-weighted dot-product loss, split-K over tokens.
+//
+// ZipMap (关键设计 1) takes one gradient over every token,
+//   G = grad_W sum_i eta_i * (-f_W(k_i)^T v_i),  f_W(x) = W2 (SiLU(W1 x) o (W3 x)),
+// with the loss of Scal3R eq. (9).  Because dL/df_i = -eta_i v_i does not depend
+// on f, the gradient needs, per token and hidden unit j,
+//   z1 = w1_j . k,  z3 = w3_j . k,  p = w2t_j . v   (forward on keys, back-projection of v)
+//   s = sigmoid(z1), a = z1 s,  dH = -eta p,
+//   dZ3 = dH a,  dZ1 = dH z3 (s + a - a s),  H' = -eta a z3
+// and the three contractions over tokens
+//   G1 = dZ1^T K,  G3 = dZ3^T K,  G2 = V^T H'.
+//
+// A workgroup owns one head, 64 hidden units (16 per wave), one output d-chunk
+// and one contiguous token range (its split); it writes fp32 partial gradients
+// that a second kernel sums in fixed split order (deterministic).
+//
+// Per 32-token block a wave computes z1, z3, p for its 16 hidden units x 32
+// tokens (MFMA, tokens as rows), applies the SwiGLU backward in registers, and
+// feeds dZ1, dZ3, H' straight back into the MFMA as operands: the tokens'
+// row order is permuted (perm_row) so that the accumulator layout of the first
+// product is the operand layout of the second, with no LDS round trip.
+#include "common.h"
+#include "kernels.h"
+
+namespace ttt {
+namespace {
+
+// ---------------------------------------------------------------- fast path
+// bf16 tokens, D <= 256: K and V blocks are staged in LDS twice (row-major for
+// the d-reductions, transposed for the token reductions), double-buffered;
+// each wave keeps its 16 rows of W1, W3, W2^T in registers.
+template <int D>
+struct FastLayout {
+  static constexpr int kRowBytes = D * 2;                 // one token row, bf16
+  static constexpr int kNatBytes = kTokBlock * kRowBytes; // one row-major tile
+  static constexpr int kTrBytes = D * kTokBlock * 2;      // one transposed tile
+  static constexpr int kStage = 2 * kNatBytes + 2 * kTrBytes;
+  // byte offsets inside a stage
+  static __device__ __forceinline__ int nat(int mat, int r, int c) {
+    return mat * kNatBytes + r * kRowBytes + 16 * (c ^ swz_rows(r));
+  }
+  static __device__ __forceinline__ int tr(int mat, int rho, int a) {
+    return 2 * kNatBytes + mat * kTrBytes + rho * 64 + 16 * (a ^ swz_64(rho));
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
+  using L = FastLayout<D>;
+  constexpr int KC = D / 32;   // reduction chunks over d
+  constexpr int DT = D / 16;   // 16-wide d tiles of the outputs
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * L::kStage];
+
+  const int total = gridDim.x;
+  const int b = blockIdx.x;
+  const int lin = p.xcd_map ? ((b & 7) * (total >> 3) + (b >> 3)) : b;
+  const int mtiles = p.m / kHidTile;
+  const int jt = lin % mtiles;
+  int grp = lin / mtiles;
+  const int h = grp % p.heads;
+  const int split = grp / p.heads;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int hid0 = jt * kHidTile + 16 * w;
+
+  // weights of this wave's 16 hidden units, B-operand fragments over d
+  bf16x8 w1f[KC], w3f[KC], w2f[KC];
+  {
+    const int64_t row = ((int64_t)h * p.m + hid0 + li) * D + 8 * g;
+    const __bf16 *W1 = static_cast<const __bf16 *>(p.w1) + row;
+    const __bf16 *W3 = static_cast<const __bf16 *>(p.w3) + row;
+    const __bf16 *W2 = static_cast<const __bf16 *>(p.w2t) + row;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      w1f[kc] = ld8(W1 + 32 * kc);
+      w3f[kc] = ld8(W3 + 32 * kc);
+      w2f[kc] = ld8(W2 + 32 * kc);
+    }
+  }
+
+  f32x4 a1[DT], a3[DT], a2[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) a1[i] = a3[i] = a2[i] = f32x4{0, 0, 0, 0};
+
+  const int64_t blk0 = (int64_t)split * p.nblk / p.splits;
+  const int64_t blk1 = (int64_t)(split + 1) * p.nblk / p.splits;
+
+  // staging role: thread -> (matrix, 8x8 block (a, c)); D/2 blocks per matrix
+  const bool stager = tid < D;
+  const int smat = tid / (D / 2);
+  const int su = tid % (D / 2);
+  const int sa = su / (D / 8), sc = su % (D / 8);
+  const __bf16 *src = static_cast<const __bf16 *>(smat ? p.v : p.k) + (int64_t)h * D + 8 * sc;
+  u32x4 raw[8];
+
+  auto load_block = [&](int64_t blk) {
+    const int64_t t0 = blk * kTokBlock + 8 * sa;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t tok = t0 + i;
+      raw[i] = (tok < p.n) ? *reinterpret_cast<const u32x4 *>(src + tok * p.ld) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_block = [&](int stage) {
+    unsigned char *base = smem + stage * L::kStage;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(base + L::nat(smat, 8 * sa + i, sc)) = raw[i];
+    u32x4 tr[8];
+    transpose8x8_b16(raw, tr);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(base + L::tr(smat, 8 * sc + j, sa)) = tr[j];
+  };
+
+  if (stager && blk0 < blk1) {
+    load_block(blk0);
+    store_block(0);
+  }
+  __syncthreads();
+
+  const float *eta = p.eta + (int64_t)h * p.eta_hs;
+  int cur = 0;
+  for (int64_t blk = blk0; blk < blk1; ++blk) {
+    const bool more = blk + 1 < blk1;
+    if (stager && more) load_block(blk + 1);
+
+    // eta of this lane's 8 tokens 8g .. 8g+7 of the block
+    float e[8];
+    {
+      const int64_t t0 = blk * kTokBlock + 8 * g;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) e[v] = (t0 + v < p.n) ? eta[t0 + v] : 0.0f;
+    }
+
+    const unsigned char *base = smem + cur * L::kStage;
+    // forward on keys and back-projection of values: rows = tokens perm_row(u, li)
+    f32x4 z1[2], z3[2], pp[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
+      const int rt = perm_row(u, li);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(base + L::nat(0, rt, 4 * kc + g));
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(base + L::nat(1, rt, 4 * kc + g));
+        z1[u] = mma(kf, w1f[kc], z1[u]);
+        z3[u] = mma(kf, w3f[kc], z3[u]);
+        pp[u] = mma(vf, w2f[kc], pp[u]);
+      }
+    }
+    // SwiGLU backward; element v = 4u + r is token 8g + v of the block, hidden hid0 + li
+    float dz1v[8], dz3v[8], hv[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * u + r;
+        const float z = z1[u][r], y = z3[u][r], ne = -e[v];
+        const float sg = sigmoid_fast(z);
+        const float act = z * sg;
+        const float dh = ne * pp[u][r];
+        dz3v[v] = dh * act;
+        dz1v[v] = dh * y * (sg + act - act * sg);
+        hv[v] = ne * (act * y);
+      }
+    const bf16x8 dz1f = pack8<__bf16>(dz1v), dz3f = pack8<__bf16>(dz3v), hf = pack8<__bf16>(hv);
+    // token contractions: G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H'
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 ktf = *reinterpret_cast<const bf16x8 *>(base + L::tr(0, 16 * dt + li, g));
+      const bf16x8 vtf = *reinterpret_cast<const bf16x8 *>(base + L::tr(1, 16 * dt + li, g));
+      a1[dt] = mma(dz1f, ktf, a1[dt]);
+      a3[dt] = mma(dz3f, ktf, a3[dt]);
+      a2[dt] = mma(vtf, hf, a2[dt]);
+    }
+    if (stager && more) store_block(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // partials: G1/G3 rows hid0 + 4g + r, cols 16 dt + li;  G2 rows 16 dt + 4g + r, cols hid0 + li
+  const int64_t mat = (int64_t)p.m * D;
+  float *P1 = p.part + ((int64_t)split * 3 * p.heads + h) * mat;
+  float *P3 = P1 + p.heads * mat;
+  float *P2 = P3 + p.heads * mat;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      P1[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a1[dt][r];
+      P3[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a3[dt][r];
+      P2[(int64_t)(16 * dt + 4 * g + r) * p.m + hid0 + li] = a2[dt][r];
+    }
+}
+
+// ------------------------------------------------------------- general path
+// Any supported d, fp32 or bf16.  The d-reductions read K, V and the weights
+// straight from global memory (L1/L2 resident); only the transposed K, V
+// columns of this workgroup's output d-chunk go through LDS.  The forward is
+// recomputed for every d-chunk.
+template <typename T, int D, int DC>
+__global__ __launch_bounds__(256) void grad_general_kernel(GradParams p) {
+  using F = typename FragOf<T>::type;
+  constexpr int KC = D / 32;
+  constexpr int DT = DC / 16;
+  constexpr int PAD = 16 / sizeof(T);         // keeps 16-byte aligned rows
+  constexpr int RS = kTokBlock + PAD;         // LDS row stride (elements)
+  __shared__ __attribute__((aligned(16))) T kt[DC * RS];
+  __shared__ __attribute__((aligned(16))) T vt[DC * RS];
+
+  const int b = blockIdx.x;
+  const int mtiles = p.m / kHidTile;
+  const int jt = b % mtiles;
+  int grp = b / mtiles;
+  const int dc = grp % p.dchunks;
+  grp /= p.dchunks;
+  const int h = grp % p.heads;
+  const int split = grp / p.heads;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int hid0 = jt * kHidTile + 16 * w;
+  const int d0 = dc * DC;
+
+  const T *K = static_cast<const T *>(p.k) + (int64_t)h * D;
+  const T *V = static_cast<const T *>(p.v) + (int64_t)h * D;
+  const int64_t wrow = ((int64_t)h * p.m + hid0 + li) * D + 8 * g;
+  const T *W1 = static_cast<const T *>(p.w1) + wrow;
+  const T *W3 = static_cast<const T *>(p.w3) + wrow;
+  const T *W2 = static_cast<const T *>(p.w2t) + wrow;
+  const float *eta = p.eta + (int64_t)h * p.eta_hs;
+
+  f32x4 a1[DT], a3[DT], a2[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) a1[i] = a3[i] = a2[i] = f32x4{0, 0, 0, 0};
+
+  const int64_t blk0 = (int64_t)split * p.nblk / p.splits;
+  const int64_t blk1 = (int64_t)(split + 1) * p.nblk / p.splits;
+  for (int64_t blk = blk0; blk < blk1; ++blk) {
+    const int64_t tb = blk * kTokBlock;
+    // stage K, V columns [d0, d0 + DC) of the block, transposed
+    for (int e = tid; e < kTokBlock * DC; e += 256) {
+      const int i = e / DC, c = e % DC;
+      const int64_t tok = tb + i;
+      const bool ok = tok < p.n;
+      kt[c * RS + i] = ok ? K[tok * p.ld + d0 + c] : from_f32<T>(0.0f);
+      vt[c * RS + i] = ok ? V[tok * p.ld + d0 + c] : from_f32<T>(0.0f);
+    }
+    float e8[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) e8[v] = (tb + 8 * g + v < p.n) ? eta[tb + 8 * g + v] : 0.0f;
+    __syncthreads();
+
+    f32x4 z1[2], z3[2], pp[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
+      const int64_t tok = tb + perm_row(u, li);
+      const bool ok = tok < p.n;
+#pragma unroll 2
+      for (int kc = 0; kc < KC; ++kc) {
+        const F kf = ok ? ld8(K + tok * p.ld + 32 * kc + 8 * g) : zero8<T>();
+        const F vf = ok ? ld8(V + tok * p.ld + 32 * kc + 8 * g) : zero8<T>();
+        z1[u] = mma(kf, ld8(W1 + 32 * kc), z1[u]);
+        z3[u] = mma(kf, ld8(W3 + 32 * kc), z3[u]);
+        pp[u] = mma(vf, ld8(W2 + 32 * kc), pp[u]);
+      }
+    }
+    float dz1v[8], dz3v[8], hv[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * u + r;
+        const float z = z1[u][r], y = z3[u][r], ne = -e8[v];
+        const float sg = sigmoid_fast(z);
+        const float act = z * sg;
+        const float dh = ne * pp[u][r];
+        dz3v[v] = dh * act;
+        dz1v[v] = dh * y * (sg + act - act * sg);
+        hv[v] = ne * (act * y);
+      }
+    const F dz1f = pack8<T>(dz1v), dz3f = pack8<T>(dz3v), hf = pack8<T>(hv);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const F ktf = ld8(&kt[(16 * dt + li) * RS + 8 * g]);
+      const F vtf = ld8(&vt[(16 * dt + li) * RS + 8 * g]);
+      a1[dt] = mma(dz1f, ktf, a1[dt]);
+      a3[dt] = mma(dz3f, ktf, a3[dt]);
+      a2[dt] = mma(vtf, hf, a2[dt]);
+    }
+    __syncthreads();
+  }
+
+  const int64_t mat = (int64_t)p.m * D;
+  float *P1 = p.part + ((int64_t)split * 3 * p.heads + h) * mat;
+  float *P3 = P1 + p.heads * mat;
+  float *P2 = P3 + p.heads * mat;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      P1[(int64_t)(hid0 + 4 * g + r) * D + d0 + 16 * dt + li] = a1[dt][r];
+      P3[(int64_t)(hid0 + 4 * g + r) * D + d0 + 16 * dt + li] = a3[dt][r];
+      P2[(int64_t)(d0 + 16 * dt + 4 * g + r) * p.m + hid0 + li] = a2[dt][r];
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_general(const GradParams &p, int grid, hipStream_t s) {
+  constexpr int DC = (sizeof(T) == 2) ? (D < 128 ? D : 128) : (D < 64 ? D : 64);
+  hipLaunchKernelGGL((grad_general_kernel<T, D, DC>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_general_d(const GradParams &p, int d, int grid, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_general<T, 64>(p, grid, s);
+    case 128: return launch_general<T, 128>(p, grid, s);
+    case 256: return launch_general<T, 256>(p, grid, s);
+    case 512: return launch_general<T, 512>(p, grid, s);
+    case 768: return launch_general<T, 768>(p, grid, s);
+    case 1024: return launch_general<T, 1024>(p, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool grad_fast_supported(int d, bool bf16) { return bf16 && (d == 64 || d == 128 || d == 256); }
+
+int grad_general_dc(int d, bool bf16) {
+  if (bf16) return d < 128 ? d : 128;
+  return d < 64 ? d : 64;
+}
+
+hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int grid, hipStream_t s) {
+  if (fast) {
+    switch (d) {
+      case 64: hipLaunchKernelGGL(grad_fast_kernel<64>, dim3(grid), dim3(256), 0, s, p); break;
+      case 128: hipLaunchKernelGGL(grad_fast_kernel<128>, dim3(grid), dim3(256), 0, s, p); break;
+      case 256: hipLaunchKernelGGL(grad_fast_kernel<256>, dim3(grid), dim3(256), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  return bf16 ? launch_general_d<__bf16>(p, d, grid, s) : launch_general_d<float>(p, d, grid, s);
+}
+
+}  // namespace ttt

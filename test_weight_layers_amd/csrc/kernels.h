@@ -1,0 +1,80 @@
+// Host-side declarations of the kernel launchers (one per .hip file).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ttt {
+
+// Token blocks of the gradient kernels: 32 tokens (one bf16 MFMA reduction step).
+constexpr int kTokBlock = 32;
+// Hidden units per gradient workgroup (4 waves x 16).
+constexpr int kHidTile = 64;
+
+struct GradParams {
+  const void *k, *v;         // [n][ld] token rows
+  int64_t ld;
+  const float *eta;          // eta[h * eta_hs + i]
+  int64_t eta_hs;
+  const void *w1, *w3;       // [H][m][d] operand-type copies (or fp32 master)
+  const void *w2t;           // [H][m][d] transposed W2
+  float *part;               // [splits][3][H][m*d] fp32 partial gradients
+  int64_t n, nblk;           // tokens, ceil(n / kTokBlock)
+  int heads, m, splits, dchunks, xcd_map;
+};
+
+struct ApplyParams {
+  const void *q;
+  int64_t ldq;
+  void *o;
+  int64_t ldo;
+  const void *w1, *w3;       // [H][m][d]
+  const void *w2;            // [H][d][m]
+  int64_t nq;
+  int heads, m, dchunks;
+};
+
+// Kernel families.  `fast` variants: bf16 tokens with d <= 256 (LDS-staged,
+// register-resident weights); `general` variants: any supported d, fp32 or bf16.
+bool grad_fast_supported(int d, bool bf16);
+int grad_general_dc(int d, bool bf16);      // output d-chunk width of the general kernel
+hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int grid, hipStream_t s);
+
+bool apply_fast_supported(int d, bool bf16);
+int apply_general_dc(int d, bool bf16);
+hipError_t launch_apply(const ApplyParams &p, int d, bool bf16, bool fast, hipStream_t s);
+
+// fp32 master W -> operand copies.  w1o/w3o: [H][m][d]; w2to: [H][m][d] (transposed W2);
+// w2o: [H][d][m].  Any output may be null.  bf16 selects the output type.
+hipError_t launch_cast(const float *w1, const float *w3, const float *w2, void *w1o, void *w3o,
+                       void *w2to, void *w2o, int heads, int d, int m, bool bf16, hipStream_t s);
+
+// Sum of split partials in fixed split order; also per-4096-element sums of squares.
+hipError_t launch_reduce(const float *part, int splits, int64_t per_split, float *g, float *g_copy,
+                         float *sumsq, hipStream_t s);
+
+struct NsShape {
+  int heads, d, m;           // matrices: 3*heads, G1/G3 [m][d], G2 [d][m]
+};
+// X = G / (||G||_F + eps), transposed to [min][max] where needed.
+hipError_t launch_ns_normalize(const float *g, const float *sumsq, float *x, const NsShape &sh,
+                               float eps, hipStream_t s);
+// Batched C = alpha * A * op(B) + beta * D over `batch` matrices (fp32 MFMA).
+struct GemmBatch {
+  const float *a, *b, *dm;
+  float *c;
+  int M, N, K, lda, ldb, ldd, ldc, b_trans;
+  int64_t sa, sb, sd, sc;
+  float alpha, beta;
+  int batch;
+};
+hipError_t launch_gemm_f32(const GemmBatch &g, hipStream_t s);
+// W_out = W_src - lr * NS (NS taken from X, undoing the transpose); optional ns copy.
+hipError_t launch_ns_step(const float *x, const float *w1, const float *w3, const float *w2, float *w1o,
+                          float *w3o, float *w2o, float *ns_out, float lr, const NsShape &sh,
+                          hipStream_t s);
+
+hipError_t launch_conv(const void *v, void *out, int64_t ld, const float *w, int frames, int tpf,
+                       int nsp, int gh, int gw, int channels, bool bf16, hipStream_t s);
+
+}  // namespace ttt

@@ -1,0 +1,220 @@
+// Split-K reduction of the gradient partials, Muon's Newton-Schulz
+// orthogonalisation and the step W <- W - lr * NS(G), plus the fp32 -> operand
+// weight copies.
+//
+// Newton-Schulz (ZipMap 关键设计 3: Delta <- NewtonSchulz(g); VGG-T3 and tttLRM
+// name the Muon optimiser): X = G / (||G||_F + eps), transposed while it has more
+// rows than columns, then five times  A = X X^T,  B = b A + c A A,  X = a X + B X
+// with Muon's quintic coefficients (a, b, c) = (3.4445, -4.7750, 2.0315).  All of
+// it runs in fp32 (fp32 MFMA); only the three small GEMMs per iteration are
+// batched over the 3*H gradient matrices.
+#include "common.h"
+#include "kernels.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kRedBlock = 4096;   // elements per reduction workgroup (256 threads x 16)
+
+__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ part, int splits,
+                                                     int64_t per_split, float *__restrict__ g,
+                                                     float *__restrict__ g_copy, float *__restrict__ sumsq) {
+  __shared__ float red[256];
+  const int64_t base = (int64_t)blockIdx.x * kRedBlock;
+  float ss = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t i = base + (int64_t)(q * 256 + threadIdx.x) * 4;
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4 *>(part + (int64_t)s * per_split + i);
+    *reinterpret_cast<f32x4 *>(g + i) = acc;
+    if (g_copy) *reinterpret_cast<f32x4 *>(g_copy + i) = acc;
+    ss += acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
+  }
+  red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sumsq[blockIdx.x] = red[0];
+}
+
+// Matrix b (0 .. 3H-1): j = b / H selects G1, G3, G2; G1/G3 are [m][d], G2 [d][m].
+// X_b is [r][c] with r = min(d, m), c = max(d, m): the transpose of G_b when G_b
+// has more rows than columns.
+__device__ __forceinline__ bool ns_transposed(int j, int d, int m) { return j < 2 ? (m > d) : (d > m); }
+
+__global__ __launch_bounds__(256) void ns_normalize_kernel(const float *__restrict__ g, const float *__restrict__ sumsq,
+                                                           float *__restrict__ x, int heads, int d, int m, float eps) {
+  const int64_t mat = (int64_t)d * m;
+  const int per = (int)(mat / kRedBlock);
+  const int64_t e0 = (int64_t)blockIdx.x * kRedBlock;
+  const int b = (int)(e0 / mat);
+  const int j = b / heads;
+  float ss = 0.0f;
+  for (int i = 0; i < per; ++i) ss += sumsq[(int64_t)b * per + i];
+  const float scale = 1.0f / (sqrtf(ss) + eps);
+  const bool tr = ns_transposed(j, d, m);
+  const int rows = j < 2 ? m : d, cols = j < 2 ? d : m;     // shape of G_b
+  const float *G = g + (int64_t)b * mat;
+  float *X = x + (int64_t)b * mat;
+  for (int q = threadIdx.x; q < kRedBlock; q += 256) {
+    const int64_t e = e0 + q - (int64_t)b * mat;            // index inside X_b
+    float val;
+    if (tr) {                                               // X = G^T: [cols][rows]
+      const int64_t xr = e / rows, xc = e % rows;
+      val = G[xc * cols + xr];
+    } else {
+      val = G[e];
+    }
+    X[e] = val * scale;
+  }
+}
+
+// 32x32 output tile per single-wave workgroup, K staged through LDS 32 at a time.
+__global__ __launch_bounds__(64) void gemm_f32_kernel(GemmBatch p) {
+  __shared__ __attribute__((aligned(16))) float as[32][36];
+  __shared__ __attribute__((aligned(16))) float bs[32][36];   // [n][k]
+  const int bz = blockIdx.z;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  const float *A = p.a + bz * p.sa;
+  const float *B = p.b + bz * p.sb;
+  const int l = threadIdx.x, g = l >> 4, li = l & 15;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x4{0, 0, 0, 0};
+
+  for (int k0 = 0; k0 < p.K; k0 += 32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = (l >> 3) + 8 * q, c4 = (l & 7) * 4;
+      *reinterpret_cast<f32x4 *>(&as[r][c4]) = *reinterpret_cast<const f32x4 *>(A + (int64_t)(i0 + r) * p.lda + k0 + c4);
+      if (p.b_trans) {
+        *reinterpret_cast<f32x4 *>(&bs[r][c4]) = *reinterpret_cast<const f32x4 *>(B + (int64_t)(j0 + r) * p.ldb + k0 + c4);
+      } else {   // B is [K][N]: row k0 + r, columns j0 + c4 .. +4 -> bs[n][k]
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(B + (int64_t)(k0 + r) * p.ldb + j0 + c4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bs[c4 + t][r] = v[t];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const f32x8 af = ld8(&as[16 * mt + li][8 * g]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma(af, ld8(&bs[16 * nt + li][8 * g]), acc[mt][nt]);
+    }
+    __syncthreads();
+  }
+  float *C = p.c + bz * p.sc;
+  const float *Dm = p.dm ? p.dm + bz * p.sd : nullptr;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 16 * mt + 4 * g + r, j = j0 + 16 * nt + li;
+        float v = p.alpha * acc[mt][nt][r];
+        if (Dm) v += p.beta * Dm[(int64_t)i * p.ldd + j];
+        C[(int64_t)i * p.ldc + j] = v;
+      }
+}
+
+__global__ __launch_bounds__(256) void ns_step_kernel(const float *__restrict__ x, const float *w1, const float *w3,
+                                                      const float *w2, float *w1o, float *w3o, float *w2o,
+                                                      float *__restrict__ ns_out, float lr, int heads, int d, int m) {
+  const int64_t mat = (int64_t)d * m;
+  const int64_t total = 3 * heads * mat;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t b = e / mat, off = e % mat;
+    const int j = (int)(b / heads), h = (int)(b % heads);
+    const int rows = j < 2 ? m : d, cols = j < 2 ? d : m;
+    float ns;
+    if (ns_transposed(j, d, m)) {      // X_b = G_b^T is [cols][rows]
+      const int64_t r = off / cols, c = off % cols;
+      ns = x[b * mat + c * rows + r];
+    } else {
+      ns = x[e];
+    }
+    const float *src = j == 0 ? w1 : (j == 1 ? w3 : w2);
+    float *dst = j == 0 ? w1o : (j == 1 ? w3o : w2o);
+    const int64_t wi = (int64_t)h * mat + off;
+    dst[wi] = src[wi] - lr * ns;
+    if (ns_out) ns_out[e] = ns;
+  }
+}
+
+// Weight copies.  W2 [H][d][m] -> W2^T [H][m][d] goes through a 32x32 LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void cast_rows_kernel(const float *__restrict__ w, T *__restrict__ o, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) o[i] = from_f32<T>(w[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_cast_kernel(const float *__restrict__ w2, T *__restrict__ w2t,
+                                                             int d, int m) {
+  __shared__ float tile[32][33];
+  const int h = blockIdx.z;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;     // rows of W2 (d), cols (m)
+  const float *src = w2 + (int64_t)h * d * m;
+  T *dst = w2t + (int64_t)h * d * m;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int r = ty; r < 32; r += 8) tile[r][tx] = src[(int64_t)(r0 + r) * m + c0 + tx];
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) dst[(int64_t)(c0 + r) * d + r0 + tx] = from_f32<T>(tile[tx][r]);
+}
+
+template <typename T>
+hipError_t cast_impl(const float *w1, const float *w3, const float *w2, void *w1o, void *w3o, void *w2to,
+                     void *w2o, int heads, int d, int m, hipStream_t s) {
+  const int64_t n = (int64_t)heads * d * m;
+  const int grid = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  if (w1o) hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid), dim3(256), 0, s, w1, static_cast<T *>(w1o), n);
+  if (w3o) hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid), dim3(256), 0, s, w3, static_cast<T *>(w3o), n);
+  if (w2o) hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid), dim3(256), 0, s, w2, static_cast<T *>(w2o), n);
+  if (w2to)
+    hipLaunchKernelGGL(transpose_cast_kernel<T>, dim3(m / 32, d / 32, heads), dim3(256), 0, s, w2,
+                       static_cast<T *>(w2to), d, m);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cast(const float *w1, const float *w3, const float *w2, void *w1o, void *w3o, void *w2to,
+                       void *w2o, int heads, int d, int m, bool bf16, hipStream_t s) {
+  return bf16 ? cast_impl<__bf16>(w1, w3, w2, w1o, w3o, w2to, w2o, heads, d, m, s)
+              : cast_impl<float>(w1, w3, w2, w1o, w3o, w2to, w2o, heads, d, m, s);
+}
+
+hipError_t launch_reduce(const float *part, int splits, int64_t per_split, float *g, float *g_copy, float *sumsq,
+                         hipStream_t s) {
+  const int64_t blocks = per_split / kRedBlock;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, per_split, g, g_copy, sumsq);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_normalize(const float *g, const float *sumsq, float *x, const NsShape &sh, float eps,
+                               hipStream_t s) {
+  const int64_t blocks = 3LL * sh.heads * sh.d * sh.m / kRedBlock;
+  hipLaunchKernelGGL(ns_normalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, sumsq, x, sh.heads, sh.d, sh.m,
+                     eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const GemmBatch &g, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(g.N / 32, g.M / 32, g.batch), dim3(64), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_step(const float *x, const float *w1, const float *w3, const float *w2, float *w1o, float *w3o,
+                          float *w2o, float *ns_out, float lr, const NsShape &sh, hipStream_t s) {
+  const int64_t total = 3LL * sh.heads * sh.d * sh.m;
+  const int grid = (int)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
+  hipLaunchKernelGGL(ns_step_kernel, dim3(grid), dim3(256), 0, s, x, w1, w3, w2, w1o, w3o, w2o, ns_out, lr, sh.heads,
+                     sh.d, sh.m);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -1,0 +1,184 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle on the same seeded inputs.
+
+Gate (relative Frobenius error per head and per matrix, on G, NS(G), W^ and O
+separately): 1e-4 when tokens are fp32, 2e-2 when tokens are bf16 (the oracle
+then runs on the same bf16-rounded inputs, upcast).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, cfg_like, gpu_layer, oracle_layer, parity_report
+from test_weight_layers_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from test_weight_layers_amd import ttt
+    ttt.load()          # raises if the library is missing: no fallback
+    ttt.set_option(ttt.OPT_FORCE_GENERAL, 0)
+    ttt.set_option(ttt.OPT_SPLITS, 0)
+    yield
+    ttt.set_option(ttt.OPT_FORCE_GENERAL, 0)
+    ttt.set_option(ttt.OPT_SPLITS, 0)
+
+
+def _check(cfg, n=None, nq_extra=None, steps=None, lr=None, general=False, splits=0):
+    from test_weight_layers_amd import ttt
+    inp = synth.make_inputs(cfg, n=n, nq_extra=nq_extra)
+    ttt.set_option(ttt.OPT_FORCE_GENERAL, 1 if general else 0)
+    ttt.set_option(ttt.OPT_SPLITS, splits)
+    try:
+        got = gpu_layer(inp, steps=steps, lr=lr)
+    finally:
+        ttt.set_option(ttt.OPT_FORCE_GENERAL, 0)
+        ttt.set_option(ttt.OPT_SPLITS, 0)
+    ref = oracle_layer(inp, steps=steps, lr=lr)
+    rep = parity_report(got, ref, cfg.heads, cfg.d)
+    worst = max(rep, key=rep.get)
+    print(f"{cfg.name} n={inp.k.shape[0]} nq={inp.q.shape[0]} general={general} worst {worst}={rep[worst]:.3e}")
+    tol = TOL[cfg.dtype]
+    bad = {k: v for k, v in rep.items() if not v <= tol}
+    assert not bad, bad
+    return got, ref, rep
+
+
+def test_c1_tiny_fp32_full():
+    from test_weight_layers_amd.configs import CONFIGS
+    _check(CONFIGS["c1"])
+
+
+def test_c1_tiny_in_bf16_mode():
+    _check(cfg_like("c1", dtype="bf16"))
+
+
+@pytest.mark.parametrize("general", [False, True])
+def test_vggt_heads_ragged_tokens(general):
+    # 4 heads x 256, hidden 512; 1000 tokens = 31 blocks of 32 + 8, Nq with a ragged tail
+    _check(cfg_like("c4", norm_v=False), n=1000, nq_extra=77, general=general)
+
+
+def test_vggt_heads_fp32_general():
+    _check(cfg_like("c4", dtype="f32"), n=700, nq_extra=5)
+
+
+@pytest.mark.parametrize("d,m", [(64, 128), (128, 256), (64, 512)])
+def test_other_fast_widths(d, m):
+    _check(cfg_like("c4", heads=2, d=d, m=m), n=777, nq_extra=3)
+
+
+def test_tttlrm_width_768_general():
+    from test_weight_layers_amd.configs import CONFIGS
+    _check(CONFIGS["c2"], n=1500, nq_extra=300)
+
+
+def test_two_inner_steps_with_conv():
+    cfg = cfg_like("c3", frames=2)
+    _check(cfg, steps=2)
+
+
+def test_many_splits_and_single_split_agree():
+    cfg = cfg_like("c4", heads=1)
+    g1, _, _ = _check(cfg, n=4000, splits=1)
+    g2, _, _ = _check(cfg, n=4000, splits=37)
+    for j in range(3):
+        assert np.max(np.abs(g1["G"][j] - g2["G"][j])) <= 1e-3 * np.max(np.abs(g1["G"][j]))
+
+
+def test_lr_zero_is_bit_exact_and_n_zero_leaves_w():
+    from test_weight_layers_amd import ttt
+    cfg = cfg_like("c4", heads=2)
+    inp = synth.to_device(synth.make_inputs(cfg, n=300, nq_extra=0), "cuda")
+    w = (inp.w1, inp.w3, inp.w2)
+    out = ttt.update(w, inp.k, inp.v, inp.eta, 0.0, 1)
+    for a, b in zip(out, w):
+        assert torch.equal(a, b)
+    g = torch.full((3 * 2 * 512 * 256,), 7.0, device="cuda")
+    ns = torch.full_like(g, 7.0)
+    out = ttt.update(w, inp.k[:0], inp.v[:0], inp.eta[:, :0], 0.01, 1, grad_out=g, ns_out=ns)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g) == 0 and torch.count_nonzero(ns) == 0
+    for a, b in zip(out, w):
+        assert torch.equal(a, b)
+
+
+def test_in_place_update_and_determinism():
+    from test_weight_layers_amd import ttt
+    cfg = cfg_like("c4", heads=2)
+    inp = synth.to_device(synth.make_inputs(cfg, n=2000, nq_extra=0), "cuda")
+    w = (inp.w1, inp.w3, inp.w2)
+    a = ttt.update(w, inp.k, inp.v, inp.eta, 0.01, 2)
+    b = ttt.update(w, inp.k, inp.v, inp.eta, 0.01, 2)
+    wc = tuple(x.clone() for x in w)
+    ttt.update(wc, inp.k, inp.v, inp.eta, 0.01, 2, out=wc)
+    for x, y, z in zip(a, b, wc):
+        assert torch.equal(x, y) and torch.equal(x, z)
+    # two single steps equal one two-step call
+    s1 = ttt.update(w, inp.k, inp.v, inp.eta, 0.01, 1)
+    s2 = ttt.update(s1, inp.k, inp.v, inp.eta, 0.01, 1)
+    for x, y in zip(a, s2):
+        assert torch.equal(x, y)
+
+
+def test_shared_eta_across_heads():
+    from test_weight_layers_amd import ttt
+    cfg = cfg_like("c4", heads=2)
+    inp = synth.make_inputs(cfg, n=500, nq_extra=0)
+    e1 = inp.eta[0].clone()
+    inp_shared = synth.LayerInputs(cfg, inp.w1, inp.w3, inp.w2, None, inp.k, inp.v, inp.q, e1.expand(2, -1))
+    ref = oracle_layer(inp_shared)
+    d = synth.to_device(inp, "cuda")
+    w_hat = ttt.update((d.w1, d.w3, d.w2), d.k, d.v, e1.cuda(), cfg.lr, 1)
+    for j in range(3):
+        got = w_hat[j].double().cpu().numpy()
+        for h in range(2):
+            den = np.linalg.norm(ref["W"][j][h] - synth.as_f64((inp.w1, inp.w3, inp.w2)[j][h]))
+            err = np.linalg.norm(got[h] - ref["W"][j][h])
+            assert err <= 2e-2 * den
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_shortconv2d_against_oracle(dtype):
+    from test_weight_layers_amd import ttt
+    cfg = cfg_like("c3", frames=3, dtype=dtype)
+    inp = synth.make_inputs(cfg)
+    geo = dict(frames=3, tokens_per_frame=cfg.tokens_per_frame, n_special=cfg.n_special,
+               grid_h=cfg.grid_h, grid_w=cfg.grid_w)
+    got = ttt.shortconv2d(inp.v.cuda(), inp.wconv.cuda(), **geo)
+    torch.cuda.synchronize()
+    ref = oracle.shortconv2d(synth.as_f64(inp.v), synth.as_f64(inp.wconv), **geo)
+    g = got.double().cpu().numpy()
+    if dtype == "f32":
+        np.testing.assert_allclose(g, ref, rtol=1e-5, atol=1e-6)
+    else:   # one bf16 rounding of the fp32 sum
+        np.testing.assert_allclose(g, ref, rtol=2 ** -8, atol=1e-6)
+    # special tokens are copied bit for bit
+    sp = np.concatenate([np.arange(f * cfg.tokens_per_frame, f * cfg.tokens_per_frame + cfg.n_special)
+                         for f in range(3)])
+    assert torch.equal(got[sp].cpu(), inp.v[sp])
+
+
+def test_stream_against_oracle():
+    from test_weight_layers_amd import ttt
+    cfg = cfg_like("c4", heads=2, d=256, m=512)
+    n, chunk = 1000, 300
+    inp = synth.make_inputs(cfg, n=n, nq_extra=0)
+    d = synth.to_device(inp, "cuda")
+    w = tuple(x.clone() for x in (d.w1, d.w3, d.w2))
+    o = ttt.stream(w, d.k, d.v, d.eta, d.q, cfg.lr, 1, chunk)
+    torch.cuda.synchronize()
+    f = lambda t: synth.as_f64(t)
+    o_ref, w_ref = oracle.stream(f(inp.w1), f(inp.w3), f(inp.w2), f(inp.k), f(inp.v), f(inp.eta), f(inp.q),
+                                 cfg.lr, 1, chunk)
+    from helpers import rel
+    assert rel(o.double().cpu().numpy(), o_ref) <= 2e-2
+    for j in range(3):
+        for h in range(2):
+            dw_ref = w_ref[j][h] - f((inp.w1, inp.w3, inp.w2)[j][h])
+            dw = w[j][h].double().cpu().numpy() - f((inp.w1, inp.w3, inp.w2)[j][h])
+            assert rel(dw, dw_ref) <= 2e-2
