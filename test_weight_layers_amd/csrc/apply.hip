@@ -34,7 +34,8 @@ template <int D>
 __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
   using L = ApplyLayout<D>;
   constexpr int KC = D / 32, DT = D / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::kBytes];
+  constexpr int NCH = 3 * 4 * D / 256;      // 16-byte chunks staged per thread per hidden chunk
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * L::kBytes];
 
   const int h = blockIdx.x % p.heads;
   const int64_t tile = blockIdx.x / p.heads;
@@ -47,9 +48,12 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int64_t tok = tok0 + 16 * t + li;
-    const __bf16 *Q = static_cast<const __bf16 *>(p.q) + tok * p.ldq + (int64_t)h * D + 8 * g;
+    const __bf16 *Q = static_cast<const __bf16 *>(p.q) + (tok < p.nq ? tok : 0) * p.ldq + (int64_t)h * D + 8 * g;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) qf[t][kc] = (tok < p.nq) ? ld8(Q + 32 * kc) : zero8<__bf16>();
+    for (int kc = 0; kc < KC; ++kc) {
+      const bf16x8 x = ld8(Q + 32 * kc);
+      qf[t][kc] = (tok < p.nq) ? x : zero8<__bf16>();
+    }
   }
   f32x4 acc[DT][2];
 #pragma unroll
@@ -59,22 +63,50 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
   const __bf16 *W3 = static_cast<const __bf16 *>(p.w3) + (int64_t)h * p.m * D;
   const __bf16 *W2 = static_cast<const __bf16 *>(p.w2) + (int64_t)h * D * p.m;
 
-  for (int hc = 0; hc < p.m / kHidChunk; ++hc) {
-    __syncthreads();
-    // stage W1, W3 rows [32 hc, 32 hc + 32) and W2 columns of the same units
-    for (int e = tid; e < 2 * kHidChunk * (D / 8); e += 256) {
-      const int mat = e / (kHidChunk * (D / 8));
-      const int rem = e % (kHidChunk * (D / 8));
-      const int r = rem / (D / 8), c = rem % (D / 8);
-      const __bf16 *src = (mat ? W3 : W1) + (int64_t)(hc * kHidChunk + r) * D + 8 * c;
-      *reinterpret_cast<u32x4 *>(smem + L::w13(mat, r, c)) = *reinterpret_cast<const u32x4 *>(src);
+  // Staging of one hidden chunk: 12*D/8... chunks of 16 bytes, NCH per thread.
+  // Chunk e < 2*32*(D/8): W1 / W3 row r, column chunk c; else W2 row rho, chunk a.
+  u32x4 pre[NCH];
+  auto load_chunk = [&](int hc) {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int e = tid + 256 * q;
+      const __bf16 *src;
+      if (e < 2 * kHidChunk * (D / 8)) {
+        const int mat = e / (kHidChunk * (D / 8)), rem = e % (kHidChunk * (D / 8));
+        src = (mat ? W3 : W1) + (int64_t)(hc * kHidChunk + rem / (D / 8)) * D + 8 * (rem % (D / 8));
+      } else {
+        const int f = e - 2 * kHidChunk * (D / 8);
+        src = W2 + (int64_t)(f >> 2) * p.m + hc * kHidChunk + 8 * (f & 3);
+      }
+      pre[q] = *reinterpret_cast<const u32x4 *>(src);
     }
-    for (int e = tid; e < D * 4; e += 256) {
-      const int rho = e >> 2, a = e & 3;
-      const __bf16 *src = W2 + (int64_t)rho * p.m + hc * kHidChunk + 8 * a;
-      *reinterpret_cast<u32x4 *>(smem + L::w2(rho, a)) = *reinterpret_cast<const u32x4 *>(src);
+  };
+  auto store_chunk = [&](int buf) {
+    unsigned char *base = smem + buf * L::kBytes;
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int e = tid + 256 * q;
+      int off;
+      if (e < 2 * kHidChunk * (D / 8)) {
+        const int mat = e / (kHidChunk * (D / 8)), rem = e % (kHidChunk * (D / 8));
+        off = L::w13(mat, rem / (D / 8), rem % (D / 8));
+      } else {
+        const int f = e - 2 * kHidChunk * (D / 8);
+        off = L::w2(f >> 2, f & 3);
+      }
+      *reinterpret_cast<u32x4 *>(base + off) = pre[q];
     }
-    __syncthreads();
+  };
+
+  const int nch = p.m / kHidChunk;
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int hc = 0; hc < nch; ++hc) {
+    const int cur = hc & 1;
+    const bool more = hc + 1 < nch;
+    if (more) load_chunk(hc + 1);
+    const unsigned char *base = smem + cur * L::kBytes;
 
     // Z^T rows = hidden perm_row(u, li) of the chunk, cols = tokens
     f32x4 z1[2][2], z3[2][2];
@@ -85,8 +117,8 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
       const int rw = perm_row(u, li);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(smem + L::w13(0, rw, 4 * kc + g));
-        const bf16x8 a3 = *reinterpret_cast<const bf16x8 *>(smem + L::w13(1, rw, 4 * kc + g));
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(base + L::w13(0, rw, 4 * kc + g));
+        const bf16x8 a3 = *reinterpret_cast<const bf16x8 *>(base + L::w13(1, rw, 4 * kc + g));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           z1[u][t] = mma(a1, qf[t][kc], z1[u][t]);
@@ -111,10 +143,12 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
     // O^T[d][tok] += W2[d][chunk] H^T
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 w2f = *reinterpret_cast<const bf16x8 *>(smem + L::w2(16 * dt + li, g));
+      const bf16x8 w2f = *reinterpret_cast<const bf16x8 *>(base + L::w2(16 * dt + li, g));
       acc[dt][0] = mma(w2f, hf[0], acc[dt][0]);
       acc[dt][1] = mma(w2f, hf[1], acc[dt][1]);
     }
+    if (more) store_chunk(cur ^ 1);
+    __syncthreads();
   }
 
   // O[tok][16 dt + 4g + r] for r = 0..3: one 8-byte store per (dt, t)

@@ -93,17 +93,26 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   const int sa = su / (D / 8), sc = su % (D / 8);
   const __bf16 *src = static_cast<const __bf16 *>(smat ? p.v : p.k) + (int64_t)h * D + 8 * sc;
   u32x4 raw[8];
+  int nvalid = 0;      // rows of the staged 8 that lie before n
 
+  // Rows past n (only in the last block) are read from row n-1 and zeroed when
+  // stored, so the loads carry no branches and no early wait; a zero K/V row
+  // contributes nothing to G.
   auto load_block = [&](int64_t blk) {
     const int64_t t0 = blk * kTokBlock + 8 * sa;
+    const int64_t left = p.n - t0;
+    nvalid = left < 0 ? 0 : (left > 8 ? 8 : (int)left);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t tok = t0 + i;
-      raw[i] = (tok < p.n) ? *reinterpret_cast<const u32x4 *>(src + tok * p.ld) : u32x4{0u, 0u, 0u, 0u};
+      raw[i] = *reinterpret_cast<const u32x4 *>(src + (tok < p.n ? tok : p.n - 1) * p.ld);
     }
   };
   auto store_block = [&](int stage) {
     unsigned char *base = smem + stage * L::kStage;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i >= nvalid) raw[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(base + L::nat(smat, 8 * sa + i, sc)) = raw[i];
     u32x4 tr[8];
@@ -118,35 +127,47 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   }
   __syncthreads();
 
+  // eta of this lane's 8 tokens 8g .. 8g+7 of a block, loaded one block ahead
   const float *eta = p.eta + (int64_t)h * p.eta_hs;
+  float en[8];
+  auto load_eta = [&](int64_t blk) {
+    const int64_t t0 = blk * kTokBlock + 8 * g;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) en[v] = eta[t0 + v < p.n ? t0 + v : p.n - 1];
+  };
+  if (blk0 < blk1) load_eta(blk0);
   int cur = 0;
   for (int64_t blk = blk0; blk < blk1; ++blk) {
     const bool more = blk + 1 < blk1;
-    if (stager && more) load_block(blk + 1);
-
-    // eta of this lane's 8 tokens 8g .. 8g+7 of the block
     float e[8];
     {
       const int64_t t0 = blk * kTokBlock + 8 * g;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) e[v] = (t0 + v < p.n) ? eta[t0 + v] : 0.0f;
+      for (int v = 0; v < 8; ++v) e[v] = (t0 + v < p.n) ? -en[v] : 0.0f;   // -eta, zero past n
     }
+    if (more) load_eta(blk + 1);
+    if (stager && more) load_block(blk + 1);
 
     const unsigned char *base = smem + cur * L::kStage;
-    // forward on keys and back-projection of values: rows = tokens perm_row(u, li)
+    // forward on keys and back-projection of values: rows = tokens perm_row(u, li);
+    // fragments are loaded one reduction chunk ahead of their MFMAs
     f32x4 z1[2], z3[2], pp[2];
+    constexpr int NA = 2 * KC;
+    bf16x8 kf[2], vf[2];
+    auto lda = [&](int i, int slot) {
+      const int u = i / KC, kc = i % KC, rt = perm_row(u, li);
+      kf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::nat(0, rt, 4 * kc + g));
+      vf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::nat(1, rt, 4 * kc + g));
+    };
+    lda(0, 0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
-      const int rt = perm_row(u, li);
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(base + L::nat(0, rt, 4 * kc + g));
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(base + L::nat(1, rt, 4 * kc + g));
-        z1[u] = mma(kf, w1f[kc], z1[u]);
-        z3[u] = mma(kf, w3f[kc], z3[u]);
-        pp[u] = mma(vf, w2f[kc], pp[u]);
-      }
+    for (int i = 0; i < NA; ++i) {
+      const int u = i / KC, kc = i % KC;
+      if (kc == 0) z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
+      if (i + 1 < NA) lda(i + 1, (i + 1) & 1);
+      z1[u] = mma(kf[i & 1], w1f[kc], z1[u]);
+      z3[u] = mma(kf[i & 1], w3f[kc], z3[u]);
+      pp[u] = mma(vf[i & 1], w2f[kc], pp[u]);
     }
     // SwiGLU backward; element v = 4u + r is token 8g + v of the block, hidden hid0 + li
     float dz1v[8], dz3v[8], hv[8];
@@ -155,7 +176,7 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = 4 * u + r;
-        const float z = z1[u][r], y = z3[u][r], ne = -e[v];
+        const float z = z1[u][r], y = z3[u][r], ne = e[v];
         const float sg = sigmoid_fast(z);
         const float act = z * sg;
         const float dh = ne * pp[u][r];
@@ -165,13 +186,18 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
       }
     const bf16x8 dz1f = pack8<__bf16>(dz1v), dz3f = pack8<__bf16>(dz3v), hf = pack8<__bf16>(hv);
     // token contractions: G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H'
+    bf16x8 ktf[2], vtf[2];
+    auto ldb = [&](int dt, int slot) {
+      ktf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::tr(0, 16 * dt + li, g));
+      vtf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::tr(1, 16 * dt + li, g));
+    };
+    ldb(0, 0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 ktf = *reinterpret_cast<const bf16x8 *>(base + L::tr(0, 16 * dt + li, g));
-      const bf16x8 vtf = *reinterpret_cast<const bf16x8 *>(base + L::tr(1, 16 * dt + li, g));
-      a1[dt] = mma(dz1f, ktf, a1[dt]);
-      a3[dt] = mma(dz3f, ktf, a3[dt]);
-      a2[dt] = mma(vtf, hf, a2[dt]);
+      if (dt + 1 < DT) ldb(dt + 1, (dt + 1) & 1);
+      a1[dt] = mma(dz1f, ktf[dt & 1], a1[dt]);
+      a3[dt] = mma(dz3f, ktf[dt & 1], a3[dt]);
+      a2[dt] = mma(vtf[dt & 1], hf, a2[dt]);
     }
     if (stager && more) store_block(cur ^ 1);
     __syncthreads();
