@@ -25,7 +25,7 @@ struct ApplyLayout {
   static constexpr int kW2 = D * kHidChunk * 2;         // W2 chunk [D][32]
   static constexpr int kBytes = 2 * kW13 + kW2;
   static __device__ __forceinline__ int w13(int mat, int r, int c) {
-    return mat * kW13 + r * kRowBytes + 16 * (c ^ swz_rows(r));
+    return mat * kW13 + r * kRowBytes + 16 * (c ^ (swz_rows(r) & (D / 8 - 1)));
   }
   static __device__ __forceinline__ int w2(int rho, int a) { return 2 * kW13 + rho * 64 + 16 * (a ^ swz_64(rho)); }
 };

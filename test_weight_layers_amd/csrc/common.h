@@ -77,27 +77,49 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 // D row 4g + r of tile u is block row 8g + 4u + r.
 __device__ __forceinline__ int perm_row(int u, int i) { return 8 * (i >> 2) + 4 * u + (i & 3); }
 
-// LDS swizzles (16-byte chunk granularity, 32 banks x 4 bytes assumed).
-// Row-major tile whose rows are >= 128 bytes: chunk c of row r lives at
-// c ^ swz_rows(r).  Conflict-free for 8 lanes reading perm_row(u, 0..7) at one chunk
-// and for 8 lanes writing 8 consecutive chunks of one row.
-__device__ __forceinline__ int swz_rows(int r) { return (r & 3) | ((r >> 1) & 4); }
-// Tile with 64-byte rows (4 chunks): chunk a of row r lives at a ^ swz_64(r).
-// Conflict-free for 8 lanes reading rows R..R+7 (R % 8 == 0) at one chunk.
+// LDS swizzles (16-byte chunk granularity).  gfx950's LDS serves 256 bytes per
+// cycle (64 banks x 4 bytes): a ds_read_b128 is served 16 lanes at a time, a
+// ds_read_b64 (also the transposing one) 32 lanes at a time, and a phase is
+// conflict-free when its lanes hit distinct bank words.
+//
+// Row-major tile with rows of >= 256 bytes: chunk c of row r lives at c ^ swz_rows(r).
+// swz_rows maps row bits (0, 1, 3, 4) one-to-one onto position bits (1, 2, 3, 0), so
+//  * 16 lanes reading rows perm_row(u, 0..15) at one chunk hit 16 positions;
+//  * 32 lanes of ds_read_b64_tr_b16 reading rows 8a + 4q + (0..3), a in {0,1} or
+//    {2,3}, at chunks 2t and 2t+1 hit 32 distinct 8-byte slots;
+//  * 16 lanes writing 16 consecutive chunks of one row hit 16 positions.
+// For narrower rows the value is masked to the row's chunk count (correct, not
+// conflict-optimised).
+__device__ __forceinline__ int swz_rows(int r) {
+  return ((r >> 4) & 1) | ((r & 3) << 1) | (((r >> 3) & 1) << 3);
+}
+// Tile with 64-byte rows (4 chunks, 4 rows per 256 bytes): chunk a of row r lives at
+// a ^ swz_64(r), a bijection on row bits (2, 3) within each r % 4 class, so 16 lanes
+// reading rows R..R+15 (R % 16 == 0) at one chunk hit 16 positions.
 __device__ __forceinline__ int swz_64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// Transpose an 8x8 block of 16-bit values held as 8 rows of 16 bytes.
-__device__ __forceinline__ void transpose8x8_b16(const u32x4 in[8], u32x4 out[8]) {
-  // Row i word w holds elements (i, 2w) in bits 0..15 and (i, 2w+1) in 16..31.
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int w = j >> 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = in[2 * q][w], b = in[2 * q + 1][w];
-      out[j][q] = (j & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-    }
-  }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element (i % 4) of
+// the 8-byte pieces addressed by lanes 4k + i/4, k = 0..3.  If lane s of the group
+// addresses row t0 + s/4, columns c0 + 4(s%4) .. +3 of a row-major 16-bit tile,
+// lane i receives rows t0 .. t0+3 of column c0 + i: a transposed 4 x 16 block.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const unsigned char *p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+// global_load_lds_dwordx4: every lane fetches 16 bytes from its own global address;
+// the wave's 64 pieces land contiguously at lds_wave_base + 16 * lane.
+__device__ __forceinline__ void copy16_to_lds(const void *gsrc, unsigned char *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(gsrc),
+                                   (__attribute__((address_space(3))) void *)(lds_wave_base), 16, 0, 0);
+}
+// Wait for this wave's outstanding global/LDS operations (vmcnt = lgkmcnt = 0).
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ bf16x8 cat8(const bf16x4 a, const bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 }  // namespace ttt

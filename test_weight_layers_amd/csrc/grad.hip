@@ -26,21 +26,20 @@ namespace ttt {
 namespace {
 
 // ---------------------------------------------------------------- fast path
-// bf16 tokens, D <= 256: K and V blocks are staged in LDS twice (row-major for
-// the d-reductions, transposed for the token reductions), double-buffered;
-// each wave keeps its 16 rows of W1, W3, W2^T in registers.
+// bf16 tokens, D <= 256.  Each 32-token block of K and V is staged once in LDS,
+// row-major and swizzled, double-buffered.  The d-reductions read it as MFMA
+// fragments with ds_read_b128; the token reductions read the same tile
+// transposed with ds_read_b64_tr_b16.  Each wave keeps its 16 rows of W1, W3 and
+// W2^T in registers.
 template <int D>
 struct FastLayout {
-  static constexpr int kRowBytes = D * 2;                 // one token row, bf16
-  static constexpr int kNatBytes = kTokBlock * kRowBytes; // one row-major tile
-  static constexpr int kTrBytes = D * kTokBlock * 2;      // one transposed tile
-  static constexpr int kStage = 2 * kNatBytes + 2 * kTrBytes;
-  // byte offsets inside a stage
-  static __device__ __forceinline__ int nat(int mat, int r, int c) {
-    return mat * kNatBytes + r * kRowBytes + 16 * (c ^ swz_rows(r));
-  }
-  static __device__ __forceinline__ int tr(int mat, int rho, int a) {
-    return 2 * kNatBytes + mat * kTrBytes + rho * 64 + 16 * (a ^ swz_64(rho));
+  static constexpr int kChunks = D / 8;                   // 16-byte chunks per token row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTile = kTokBlock * kRowBytes;     // one K or V block
+  static constexpr int kStage = 2 * kTile;
+  // byte offset of chunk c of row r of matrix mat (0 = K, 1 = V)
+  static __device__ __forceinline__ int at(int mat, int r, int c) {
+    return mat * kTile + r * kRowBytes + 16 * (c ^ (swz_rows(r) & (kChunks - 1)));
   }
 };
 
@@ -49,6 +48,7 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   using L = FastLayout<D>;
   constexpr int KC = D / 32;   // reduction chunks over d
   constexpr int DT = D / 16;   // 16-wide d tiles of the outputs
+  constexpr int NST = 2 * kTokBlock * (D / 8) / 256;   // chunks staged per thread per block
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * L::kStage];
 
   const int total = gridDim.x;
@@ -86,67 +86,92 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   const int64_t blk0 = (int64_t)split * p.nblk / p.splits;
   const int64_t blk1 = (int64_t)(split + 1) * p.nblk / p.splits;
 
-  // staging role: thread -> (matrix, 8x8 block (a, c)); D/2 blocks per matrix
-  const bool stager = tid < D;
-  const int smat = tid / (D / 2);
-  const int su = tid % (D / 2);
-  const int sa = su / (D / 8), sc = su % (D / 8);
-  const __bf16 *src = static_cast<const __bf16 *>(smat ? p.v : p.k) + (int64_t)h * D + 8 * sc;
-  u32x4 raw[8];
-  int nvalid = 0;      // rows of the staged 8 that lie before n
-
-  // Rows past n (only in the last block) are read from row n-1 and zeroed when
-  // stored, so the loads carry no branches and no early wait; a zero K/V row
-  // contributes nothing to G.
-  auto load_block = [&](int64_t blk) {
-    const int64_t t0 = blk * kTokBlock + 8 * sa;
-    const int64_t left = p.n - t0;
-    nvalid = left < 0 ? 0 : (left > 8 ? 8 : (int)left);
+  // Staging: each wave instruction DMAs 1 KB (64 lanes x 16 bytes) of a block
+  // straight into LDS.  1 KB piece b of a stage holds matrix b / (NPIECE / 2) and
+  // rows kRowsPer * (b % (NPIECE / 2)) ..; lane l fills row r = first + l / kChunks at
+  // physical chunk p = l % kChunks, i.e. the logical chunk p ^ swizzle(r) of token
+  // row r.  Rows past n are fetched from row n-1; their rate eta is set to 0, which
+  // zeroes dH, dZ1, dZ3 and H' and so their whole contribution.
+  constexpr int kRowsPer = 1024 / L::kRowBytes;           // token rows per 1 KB piece
+  constexpr int NPIECE = L::kStage / 1024;                // pieces per stage
+  constexpr int PPW = NPIECE / 4;                         // pieces per wave
+  const __bf16 *Kh = static_cast<const __bf16 *>(p.k) + (int64_t)h * D;
+  const __bf16 *Vh = static_cast<const __bf16 *>(p.v) + (int64_t)h * D;
+  // per-lane row and element offset (logical chunk) of each of the wave's pieces
+  int srow[PPW], soff[PPW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t tok = t0 + i;
-      raw[i] = *reinterpret_cast<const u32x4 *>(src + (tok < p.n ? tok : p.n - 1) * p.ld);
+  for (int q = 0; q < PPW; ++q) {
+    const int piece = w * PPW + q;
+    const int r = kRowsPer * (piece % (NPIECE / 2)) + l / L::kChunks;
+    srow[q] = r;
+    soff[q] = 8 * ((l % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)));
+  }
+  auto stage_block = [&](int64_t blk, int stage) {
+    const int64_t t0 = blk * kTokBlock;
+    const __bf16 *kb = Kh + t0 * p.ld, *vb = Vh + t0 * p.ld;   // wave-uniform
+    const bool full = t0 + kTokBlock <= p.n;                   // wave-uniform
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) {
+      const int piece = w * PPW + q;
+      const bool isv = piece >= NPIECE / 2;
+      int r = srow[q];
+      if (!full && t0 + r >= p.n) r = (int)(p.n - 1 - t0);
+      copy16_to_lds((isv ? vb : kb) + (int64_t)r * p.ld + soff[q], smem + stage * L::kStage + piece * 1024);
     }
   };
-  auto store_block = [&](int stage) {
-    unsigned char *base = smem + stage * L::kStage;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i >= nvalid) raw[i] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(base + L::nat(smat, 8 * sa + i, sc)) = raw[i];
-    u32x4 tr[8];
-    transpose8x8_b16(raw, tr);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(base + L::tr(smat, 8 * sc + j, sa)) = tr[j];
-  };
 
-  if (stager && blk0 < blk1) {
-    load_block(blk0);
-    store_block(0);
-  }
-  __syncthreads();
-
-  // eta of this lane's 8 tokens 8g .. 8g+7 of a block, loaded one block ahead
+  // eta of this lane's 8 tokens 8g .. 8g+7 of a block (0 past n), loaded one block ahead
   const float *eta = p.eta + (int64_t)h * p.eta_hs;
   float en[8];
   auto load_eta = [&](int64_t blk) {
     const int64_t t0 = blk * kTokBlock + 8 * g;
+    if (blk * kTokBlock + kTokBlock <= p.n) {                   // wave-uniform: block is full
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(eta + t0);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(eta + t0 + 4);
 #pragma unroll
-    for (int v = 0; v < 8; ++v) en[v] = eta[t0 + v < p.n ? t0 + v : p.n - 1];
+      for (int v = 0; v < 4; ++v) en[v] = a[v], en[4 + v] = b[v];
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) en[v] = (t0 + v < p.n) ? eta[t0 + v] : 0.0f;
+    }
   };
-  if (blk0 < blk1) load_eta(blk0);
+  if (blk0 < blk1) {
+    load_eta(blk0);
+    stage_block(blk0, 0);
+  }
+  wait_all_memory();
+  __syncthreads();
+
+  // LDS addresses.  Chunk indices 4kc + g (d-reductions) and 2dt + e (token
+  // reductions) share no bits with the loop counter's XOR partner, so with the
+  // swizzle s of a row:  ((4kc + g) ^ s) * 16 = (16 (g ^ s)) ^ 64 kc  and
+  // ((2dt + e) ^ s) * 16 = (16 (e ^ s)) ^ 32 dt: one XOR per read.
+  // d-reductions: row perm_row(u, li), chunk 4kc + g.
+  int base_a[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int rt = perm_row(u, li);
+    base_a[u] = rt * L::kRowBytes + 16 * (g ^ (swz_rows(rt) & (L::kChunks - 1)));
+  }
+  // token reductions (transposed reads): lane (g, li) supplies row 8g + 4q + li/4,
+  // column 16 dt + 4 (li % 4) and receives rows 8g + 4q .. +3 of column 16 dt + li.
+  int base_b[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 8 * g + 4 * q + (li >> 2);
+    const int e = (li & 3) >> 1;
+    base_b[q] = row * L::kRowBytes + 16 * (e ^ (swz_rows(row) & (L::kChunks - 1))) + 8 * (li & 1);
+  }
   int cur = 0;
   for (int64_t blk = blk0; blk < blk1; ++blk) {
     const bool more = blk + 1 < blk1;
-    float e[8];
-    {
-      const int64_t t0 = blk * kTokBlock + 8 * g;
+    float e[8];                                               // -eta (0 past n)
 #pragma unroll
-      for (int v = 0; v < 8; ++v) e[v] = (t0 + v < p.n) ? -en[v] : 0.0f;   // -eta, zero past n
+    for (int v = 0; v < 8; ++v) e[v] = -en[v];
+    if (more) {
+      load_eta(blk + 1);
+      stage_block(blk + 1, cur ^ 1);
     }
-    if (more) load_eta(blk + 1);
-    if (stager && more) load_block(blk + 1);
 
     const unsigned char *base = smem + cur * L::kStage;
     // forward on keys and back-projection of values: rows = tokens perm_row(u, li);
@@ -155,9 +180,10 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
     constexpr int NA = 2 * KC;
     bf16x8 kf[2], vf[2];
     auto lda = [&](int i, int slot) {
-      const int u = i / KC, kc = i % KC, rt = perm_row(u, li);
-      kf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::nat(0, rt, 4 * kc + g));
-      vf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::nat(1, rt, 4 * kc + g));
+      const int u = i / KC, kc = i % KC;
+      const unsigned char *pk = base + (base_a[u] ^ (64 * kc));
+      kf[slot] = *reinterpret_cast<const bf16x8 *>(pk);
+      vf[slot] = *reinterpret_cast<const bf16x8 *>(pk + L::kTile);
     };
     lda(0, 0);
 #pragma unroll
@@ -188,8 +214,10 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
     // token contractions: G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H'
     bf16x8 ktf[2], vtf[2];
     auto ldb = [&](int dt, int slot) {
-      ktf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::tr(0, 16 * dt + li, g));
-      vtf[slot] = *reinterpret_cast<const bf16x8 *>(base + L::tr(1, 16 * dt + li, g));
+      const unsigned char *p0 = base + (base_b[0] ^ (32 * dt));
+      const unsigned char *p1 = base + (base_b[1] ^ (32 * dt));
+      ktf[slot] = cat8(lds_read_tr16(p0), lds_read_tr16(p1));
+      vtf[slot] = cat8(lds_read_tr16(p0 + L::kTile), lds_read_tr16(p1 + L::kTile));
     };
     ldb(0, 0);
 #pragma unroll
@@ -199,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
       a3[dt] = mma(dz3f, ktf[dt & 1], a3[dt]);
       a2[dt] = mma(vtf[dt & 1], hf, a2[dt]);
     }
-    if (stager && more) store_block(cur ^ 1);
+    wait_all_memory();
     __syncthreads();
     cur ^= 1;
   }
