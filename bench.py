@@ -33,12 +33,34 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c5a")
     ap.add_argument("--frames", type=int, default=0, help="override the workload's frame count")
-    ap.add_argument("--cpu-sample-frames", type=int, default=48)
+    ap.add_argument("--cpu-sample-frames", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     ap.add_argument("--no-profile-events", action="store_true")
     return ap.parse_args()
+
+
+def measured_traffic(d):
+    """HBM bytes per launch of the gradient kernel from the committed rocprofv3 counter summary,
+    or None when the kernel's source changed since the counters were taken (or d differs)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "lact_c5a_hbm_traffic.md")
+    if d != 256 or not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ("grad.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "test_weight_layers_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    rec = {}
+    for line in open(path):
+        if line.startswith("traffic_bytes_per_launch grad_fast_kernel<256>:"):
+            rec["bytes"] = float(line.split(":")[1])
+        elif line.startswith("source_sha256 grad.hip+common.h+kernels.h:"):
+            rec["sha"] = line.split(":")[1].strip()
+    if rec.get("sha") != h.hexdigest():
+        return None
+    return rec.get("bytes")
 
 
 def flops(cfg, n, nq):
@@ -81,12 +103,16 @@ def cpu_baseline(cfg, frames):
         conv = dict(wconv=f32(inp.wconv), frames=frames, tokens_per_frame=cfg.tokens_per_frame,
                     n_special=cfg.n_special, grid_h=cfg.grid_h, grid_w=cfg.grid_w)
     t0 = time.perf_counter()
-    oracle.layer(*args, cfg.lr, cfg.steps, conv=conv)
+    if cfg.chunk_frames:
+        oracle.stream(*args, cfg.lr, cfg.steps, chunk=cfg.chunk_frames * cfg.tokens_per_frame)
+    else:
+        oracle.layer(*args, cfg.lr, cfg.steps, conv=conv)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{frames} frames x {cfg.tokens_per_frame} tokens = {n} tokens of {cfg.name}, "
-                      f"fp32 NumPy oracle, full layer (conv={cfg.conv}, steps={cfg.steps}, apply), "
+                      f"fp32 NumPy oracle, full layer (conv={cfg.conv}, steps={cfg.steps}, apply"
+                      f"{', streamed in chunks' if cfg.chunk_frames else ''}), "
                       f"{dt:.2f} s wall"}
 
 
@@ -106,8 +132,6 @@ def main():
     cfg = CONFIGS[args.config]
     if args.frames:
         cfg = cfg.with_frames(args.frames)
-    if cfg.chunk_frames:
-        raise SystemExit("streaming workloads are timed by bench_stream (not in this script)")
     torch.cuda.set_device(0)
     ttt.load()
     t_gen = time.perf_counter()
@@ -120,19 +144,29 @@ def main():
                grid_h=cfg.grid_h, grid_w=cfg.grid_w)
     w0 = (inp.w1, inp.w3, inp.w2)
     w_out = tuple(torch.empty_like(x) for x in w0)
-    v2 = torch.empty_like(inp.v)
     o = torch.empty((nq, H * d), dtype=dt, device="cuda")
-    ws_u = torch.empty(ttt.update_workspace_bytes(H, d, m, n, dt), dtype=torch.uint8, device="cuda")
-    nws = ttt.apply_workspace_bytes(H, d, m, nq, dt)
-    ws_a = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    chunk = cfg.chunk_frames * cfg.tokens_per_frame
+    if chunk:
+        # causal stream: per chunk apply with the current W, then update W from the chunk
+        ws = torch.empty(ttt.stream_workspace_bytes(H, d, m, chunk, dt), dtype=torch.uint8, device="cuda")
 
-    def step():
-        v = inp.v
-        if cfg.conv:
-            ttt.shortconv2d(inp.v, inp.wconv, **geo, out=v2)
-            v = v2
-        ttt.update(w0, inp.k, v, inp.eta, cfg.lr, cfg.steps, out=w_out, workspace=ws_u)
-        ttt.apply(w_out, inp.q, out=o, workspace=ws_a)
+        def step():
+            for a, b in zip(w_out, w0):
+                a.copy_(b)
+            ttt.stream(w_out, inp.k, inp.v, inp.eta, inp.q, cfg.lr, cfg.steps, chunk, out=o, workspace=ws)
+    else:
+        v2 = torch.empty_like(inp.v)
+        ws_u = torch.empty(ttt.update_workspace_bytes(H, d, m, n, dt), dtype=torch.uint8, device="cuda")
+        nws = ttt.apply_workspace_bytes(H, d, m, nq, dt)
+        ws_a = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+
+        def step():
+            v = inp.v
+            if cfg.conv:
+                ttt.shortconv2d(inp.v, inp.wconv, **geo, out=v2)
+                v = v2
+            ttt.update(w0, inp.k, v, inp.eta, cfg.lr, cfg.steps, out=w_out, workspace=ws_u)
+            ttt.apply(w_out, inp.q, out=o, workspace=ws_a)
 
     for _ in range(args.warmup):
         step()
@@ -151,6 +185,11 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
 
     grad_f, apply_f, ns_f, conv_f = flops(cfg, n, nq)
+    updates_per_step = 1
+    grad_launch_f = grad_f
+    if chunk:   # one update (and one Newton-Schulz) per chunk
+        updates_per_step = (n + chunk - 1) // chunk
+        grad_launch_f = flops(cfg, chunk, 0)[0]
     value = n * args.steps / elapsed
     out = {
         "metric": "TTT layer tokens/sec (update+apply) on 1 MI355X; % dense-bf16 MFMA peak",
@@ -160,7 +199,8 @@ def main():
         "random-init fast weights)",
         "config": {"workload": cfg.name, "frames": cfg.frames, "tokens_per_frame": cfg.tokens_per_frame,
                    "update_tokens": n, "apply_tokens": nq, "heads": H, "d": d, "hidden": m,
-                   "inner_steps": cfg.steps, "shortconv2d": cfg.conv, "lr": cfg.lr},
+                   "inner_steps": cfg.steps, "shortconv2d": cfg.conv, "lr": cfg.lr,
+                   "stream_chunk_tokens": chunk or None},
         "input_gen_s": round(gen_s, 2),
     }
     peak = PEAK_BF16_TFLOPS if dt == torch.bfloat16 else PEAK_F32_TFLOPS
@@ -172,16 +212,20 @@ def main():
         out["kernels"] = per_kernel
         gemm_flops = (grad_f * cfg.steps + apply_f) * args.steps
         out["mfma_pct_gemm_phases"] = 100.0 * gemm_flops / ((g_ms + a_ms) * 1e-3) / (peak * 1e12)
-        out["mfma_pct_whole_layer"] = 100.0 * (gemm_flops + ns_f * cfg.steps * args.steps) / elapsed / (peak * 1e12)
+        out["mfma_pct_whole_layer"] = (100.0 * (gemm_flops + ns_f * cfg.steps * updates_per_step * args.steps)
+                                       / elapsed / (peak * 1e12))
         grad_avg_s = g_ms * 1e-3 / g_n
-        achieved = grad_f / grad_avg_s / 1e12
+        achieved = grad_launch_f / grad_avg_s / 1e12
         out["roofline"] = {"bound": "mfma", "kernel": "grad (fused forward + SwiGLU backward + weight-gradient "
                            "contractions)", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                           "frac": achieved / peak, "traffic": None,
-                           "avg_launch_ms": grad_avg_s * 1e3, "flop_per_launch": grad_f}
+                           "frac": achieved / peak,
+                           "traffic": measured_traffic(d) if cfg.name.startswith("c5a") else None,
+                           "avg_launch_ms": grad_avg_s * 1e3, "flop_per_launch": grad_launch_f}
         if a_n:
             a_avg = a_ms * 1e-3 / a_n
-            out["apply_kernel"] = {"achieved_tflops": apply_f / a_avg / 1e12, "frac": apply_f / a_avg / 1e12 / peak,
+            apply_launch_f = apply_f * args.steps / a_n
+            out["apply_kernel"] = {"achieved_tflops": apply_launch_f / a_avg / 1e12,
+                                   "frac": apply_launch_f / a_avg / 1e12 / peak,
                                    "avg_launch_ms": a_avg * 1e3}
         if cfg.conv and kt["conv"][1]:
             c_avg = kt["conv"][0] * 1e-3 / kt["conv"][1]
