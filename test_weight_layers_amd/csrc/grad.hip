@@ -26,21 +26,22 @@ namespace ttt {
 namespace {
 
 // ---------------------------------------------------------------- fast path
-// bf16 tokens, D <= 256.  Each 32-token block of K and V is staged once in LDS,
-// row-major and swizzled, double-buffered.  The d-reductions read it as MFMA
-// fragments with ds_read_b128; the token reductions read the same tile
+// bf16 tokens, D <= 256.  Each 32-token block of K and V is DMA'd into LDS once,
+// row-major and swizzled, into one of three stages.  The d-reductions read it as
+// MFMA fragments with ds_read_b128; the token reductions read the same tile
 // transposed with ds_read_b64_tr_b16.  Each wave keeps its 16 rows of W1, W3 and
 // W2^T in registers.
+//
+// Software pipeline over blocks: iteration i runs the d-reductions of block i,
+// then the SwiGLU backward of block i (VALU) interleaved with the token
+// contractions of block i-1 (MFMA), while block i+1 streams into the third stage.
 template <int D>
 struct FastLayout {
   static constexpr int kChunks = D / 8;                   // 16-byte chunks per token row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTile = kTokBlock * kRowBytes;     // one K or V block
   static constexpr int kStage = 2 * kTile;
-  // byte offset of chunk c of row r of matrix mat (0 = K, 1 = V)
-  static __device__ __forceinline__ int at(int mat, int r, int c) {
-    return mat * kTile + r * kRowBytes + 16 * (c ^ (swz_rows(r) & (kChunks - 1)));
-  }
+  static constexpr int kStages = 3;
 };
 
 template <int D>
@@ -48,8 +49,11 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   using L = FastLayout<D>;
   constexpr int KC = D / 32;   // reduction chunks over d
   constexpr int DT = D / 16;   // 16-wide d tiles of the outputs
-  constexpr int NST = 2 * kTokBlock * (D / 8) / 256;   // chunks staged per thread per block
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * L::kStage];
+  // three separate arrays (not one indexed array) so that the compiler can tell the
+  // stage being DMA'd from the two being read and need not wait for the DMA
+  __shared__ __attribute__((aligned(16))) unsigned char st0[L::kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[L::kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[L::kStage];
 
   const int total = gridDim.x;
   const int b = blockIdx.x;
@@ -97,7 +101,6 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   constexpr int PPW = NPIECE / 4;                         // pieces per wave
   const __bf16 *Kh = static_cast<const __bf16 *>(p.k) + (int64_t)h * D;
   const __bf16 *Vh = static_cast<const __bf16 *>(p.v) + (int64_t)h * D;
-  // per-lane row and element offset (logical chunk) of each of the wave's pieces
   int srow[PPW], soff[PPW];
 #pragma unroll
   for (int q = 0; q < PPW; ++q) {
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
     srow[q] = r;
     soff[q] = 8 * ((l % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)));
   }
-  auto stage_block = [&](int64_t blk, int stage) {
+  auto stage_block = [&](int64_t blk, unsigned char *dst) {
     const int64_t t0 = blk * kTokBlock;
     const __bf16 *kb = Kh + t0 * p.ld, *vb = Vh + t0 * p.ld;   // wave-uniform
     const bool full = t0 + kTokBlock <= p.n;                   // wave-uniform
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
       const bool isv = piece >= NPIECE / 2;
       int r = srow[q];
       if (!full && t0 + r >= p.n) r = (int)(p.n - 1 - t0);
-      copy16_to_lds((isv ? vb : kb) + (int64_t)r * p.ld + soff[q], smem + stage * L::kStage + piece * 1024);
+      copy16_to_lds((isv ? vb : kb) + (int64_t)r * p.ld + soff[q], dst + piece * 1024);
     }
   };
 
@@ -135,12 +138,6 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
       for (int v = 0; v < 8; ++v) en[v] = (t0 + v < p.n) ? eta[t0 + v] : 0.0f;
     }
   };
-  if (blk0 < blk1) {
-    load_eta(blk0);
-    stage_block(blk0, 0);
-  }
-  wait_all_memory();
-  __syncthreads();
 
   // LDS addresses.  Chunk indices 4kc + g (d-reductions) and 2dt + e (token
   // reductions) share no bits with the loop counter's XOR partner, so with the
@@ -162,21 +159,11 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
     const int e = (li & 3) >> 1;
     base_b[q] = row * L::kRowBytes + 16 * (e ^ (swz_rows(row) & (L::kChunks - 1))) + 8 * (li & 1);
   }
-  int cur = 0;
-  for (int64_t blk = blk0; blk < blk1; ++blk) {
-    const bool more = blk + 1 < blk1;
-    float e[8];                                               // -eta (0 past n)
-#pragma unroll
-    for (int v = 0; v < 8; ++v) e[v] = -en[v];
-    if (more) {
-      load_eta(blk + 1);
-      stage_block(blk + 1, cur ^ 1);
-    }
 
-    const unsigned char *base = smem + cur * L::kStage;
-    // forward on keys and back-projection of values: rows = tokens perm_row(u, li);
-    // fragments are loaded one reduction chunk ahead of their MFMAs
-    f32x4 z1[2], z3[2], pp[2];
+  // d-reductions of one block: z1 = K W1^T, z3 = K W3^T, p = V W2 for this wave's
+  // 16 hidden units; rows = tokens perm_row(u, li); fragments one chunk ahead
+  f32x4 z1[2], z3[2], pp[2];
+  auto forward = [&](const unsigned char *base) {
     constexpr int NA = 2 * KC;
     bf16x8 kf[2], vf[2];
     auto lda = [&](int i, int slot) {
@@ -195,23 +182,23 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
       z3[u] = mma(kf[i & 1], w3f[kc], z3[u]);
       pp[u] = mma(vf[i & 1], w2f[kc], pp[u]);
     }
-    // SwiGLU backward; element v = 4u + r is token 8g + v of the block, hidden hid0 + li
-    float dz1v[8], dz3v[8], hv[8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = 4 * u + r;
-        const float z = z1[u][r], y = z3[u][r], ne = e[v];
-        const float sg = sigmoid_fast(z);
-        const float act = z * sg;
-        const float dh = ne * pp[u][r];
-        dz3v[v] = dh * act;
-        dz1v[v] = dh * y * (sg + act - act * sg);
-        hv[v] = ne * (act * y);
-      }
-    const bf16x8 dz1f = pack8<__bf16>(dz1v), dz3f = pack8<__bf16>(dz3v), hf = pack8<__bf16>(hv);
-    // token contractions: G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H'
+  };
+  // SwiGLU backward of element v = 4u + r (token 8g + v, hidden hid0 + li)
+  float dz1v[8], dz3v[8], hv[8];
+  auto backward_elem = [&](int v, const float *e) {
+    const int u = v >> 2, r = v & 3;
+    const float z = z1[u][r], y = z3[u][r], ne = e[v];
+    const float sg = sigmoid_fast(z);
+    const float act = z * sg;
+    const float dh = ne * pp[u][r];
+    dz3v[v] = dh * act;
+    dz1v[v] = dh * y * (sg + act - act * sg);
+    hv[v] = ne * (act * y);
+  };
+  // token contractions of a block: G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H', with
+  // the SwiGLU backward of the next block (if any) interleaved between the MFMAs
+  bf16x8 dz1f, dz3f, hf;
+  auto contract = [&](const unsigned char *base, bool with_backward, const float *e) {
     bf16x8 ktf[2], vtf[2];
     auto ldb = [&](int dt, int slot) {
       const unsigned char *p0 = base + (base_b[0] ^ (32 * dt));
@@ -226,10 +213,55 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
       a1[dt] = mma(dz1f, ktf[dt & 1], a1[dt]);
       a3[dt] = mma(dz3f, ktf[dt & 1], a3[dt]);
       a2[dt] = mma(vtf[dt & 1], hf, a2[dt]);
+      if (with_backward)   // the 8 backward elements spread evenly over the DT steps
+#pragma unroll
+        for (int v = dt * 8 / DT; v < (dt + 1) * 8 / DT; ++v) backward_elem(v, e);
     }
+  };
+  auto pack = [&]() {
+    dz1f = pack8<__bf16>(dz1v);
+    dz3f = pack8<__bf16>(dz3v);
+    hf = pack8<__bf16>(hv);
+  };
+
+  if (blk0 < blk1) {
+    load_eta(blk0);
+    stage_block(blk0, st0);
+    if (blk0 + 1 < blk1) stage_block(blk0 + 1, st1);
     wait_all_memory();
     __syncthreads();
-    cur ^= 1;
+    // prologue: forward and backward of the first block
+    float e[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) e[v] = -en[v];
+    if (blk0 + 1 < blk1) load_eta(blk0 + 1);
+    forward(st0);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) backward_elem(v, e);
+    pack();
+    // block blk lives in stage (blk - blk0) % 3
+    auto iteration = [&](int64_t blk, const unsigned char *cur, const unsigned char *prev, unsigned char *next) {
+      // consume the prefetched rates before issuing new memory operations, so that
+      // no wait for them can also wait for the DMA issued below
+#pragma unroll
+      for (int v = 0; v < 8; ++v) e[v] = -en[v];
+      if (blk + 1 < blk1) {
+        load_eta(blk + 1);
+        stage_block(blk + 1, next);     // into the stage freed by block blk-2
+      }
+      forward(cur);
+      contract(prev, true, e);          // block blk-1's contractions + block blk's backward
+      pack();
+      wait_all_memory();
+      __syncthreads();
+    };
+    for (int64_t blk = blk0 + 1; blk < blk1; blk += 3) {
+      iteration(blk, st1, st0, st2);
+      if (blk + 1 < blk1) iteration(blk + 1, st2, st1, st0);
+      if (blk + 2 < blk1) iteration(blk + 2, st0, st2, st1);
+    }
+    const int last = (int)((blk1 - 1 - blk0) % 3);
+    contract(last == 0 ? st0 : (last == 1 ? st1 : st2), false, e);
   }
 
   // partials: G1/G3 rows hid0 + 4g + r, cols 16 dt + li;  G2 rows 16 dt + 4g + r, cols hid0 + li
