@@ -101,25 +101,34 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   constexpr int PPW = NPIECE / 4;                         // pieces per wave
   const __bf16 *Kh = static_cast<const __bf16 *>(p.k) + (int64_t)h * D;
   const __bf16 *Vh = static_cast<const __bf16 *>(p.v) + (int64_t)h * D;
+  // per-lane byte offset of each piece inside a block (row r, logical chunk) and its row
   int srow[PPW], soff[PPW];
 #pragma unroll
   for (int q = 0; q < PPW; ++q) {
     const int piece = w * PPW + q;
     const int r = kRowsPer * (piece % (NPIECE / 2)) + l / L::kChunks;
     srow[q] = r;
-    soff[q] = 8 * ((l % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)));
+    soff[q] = (int)(((int64_t)r * p.ld + 8 * ((l % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)))) * 2);
   }
   auto stage_block = [&](int64_t blk, unsigned char *dst) {
     const int64_t t0 = blk * kTokBlock;
-    const __bf16 *kb = Kh + t0 * p.ld, *vb = Vh + t0 * p.ld;   // wave-uniform
-    const bool full = t0 + kTokBlock <= p.n;                   // wave-uniform
+    // wave-uniform block bases; per-lane 32-bit offsets (a block spans 32 rows)
+    const char *kb = reinterpret_cast<const char *>(Kh + t0 * p.ld);
+    const char *vb = reinterpret_cast<const char *>(Vh + t0 * p.ld);
+    if (t0 + kTokBlock <= p.n) {                                  // wave-uniform: full block
 #pragma unroll
-    for (int q = 0; q < PPW; ++q) {
-      const int piece = w * PPW + q;
-      const bool isv = piece >= NPIECE / 2;
-      int r = srow[q];
-      if (!full && t0 + r >= p.n) r = (int)(p.n - 1 - t0);
-      copy16_to_lds((isv ? vb : kb) + (int64_t)r * p.ld + soff[q], dst + piece * 1024);
+      for (int q = 0; q < PPW; ++q) {
+        const int piece = w * PPW + q;
+        copy16_to_lds((piece >= NPIECE / 2 ? vb : kb) + soff[q], dst + piece * 1024);
+      }
+    } else {                                                      // last block: clamp rows to n-1
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) {
+        const int piece = w * PPW + q;
+        const int r = srow[q];
+        const int64_t shift = (t0 + r < p.n) ? 0 : (p.n - 1 - t0 - r) * p.ld * 2;
+        copy16_to_lds((piece >= NPIECE / 2 ? vb : kb) + soff[q] + shift, dst + piece * 1024);
+      }
     }
   };
 
