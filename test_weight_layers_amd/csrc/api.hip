@@ -245,13 +245,15 @@ int do_apply(int H, int d, int m, W3 w, const void *q, int64_t ldq, void *o, int
   ap.q = q, ap.ldq = ldq, ap.o = o, ap.ldo = ldo, ap.nq = nq, ap.heads = H, ap.m = m;
   ap.dchunks = fast ? 1 : d / apply_general_dc(d, bf16);
   if (bf16) {
+    // the fast kernel reads W2 transposed ([H][m][d]), the general one as stored
     const size_t mat = (size_t)H * d * m;
     __bf16 *b = reinterpret_cast<__bf16 *>(ws);
     const int st = run(TTT_K_CAST, "cast", s, [&] {
-      return launch_cast(w.w1, w.w3, w.w2, b, b + mat, nullptr, b + 2 * mat, H, d, m, true, s);
+      return launch_cast(w.w1, w.w3, w.w2, b, b + mat, fast ? b + 2 * mat : nullptr, fast ? nullptr : b + 2 * mat, H,
+                         d, m, true, s);
     });
     if (st) return st;
-    ap.w1 = b, ap.w3 = b + mat, ap.w2 = b + 2 * mat;
+    ap.w1 = b, ap.w3 = b + mat, ap.w2 = b + 2 * mat, ap.w2t = b + 2 * mat;
   } else {
     ap.w1 = w.w1, ap.w3 = w.w3, ap.w2 = w.w2;
   }

@@ -15,27 +15,27 @@ namespace {
 constexpr int kHidChunk = 32;
 
 // ---------------------------------------------------------------- fast path
-// bf16, D <= 256.  A workgroup owns 128 tokens of one head (32 per wave) and
-// streams the head's weights through LDS 32 hidden units at a time; each wave
-// keeps its Q fragments and its O^T accumulators in registers.
+// bf16, D <= 256.  A workgroup owns 128 tokens of one head (32 per wave); each
+// wave keeps its Q fragments and its O^T accumulators in registers.  The head's
+// weights stream through LDS 32 hidden units at a time: W1 and W3 rows and W2^T
+// rows ([hidden][d], so the second product reads them with the transposing load),
+// DMA'd into one of two separate stage arrays while the other is consumed.
 template <int D>
 struct ApplyLayout {
+  static constexpr int kChunks = D / 8;
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kW13 = kHidChunk * kRowBytes;   // one W1 / W3 chunk [32][D]
-  static constexpr int kW2 = D * kHidChunk * 2;         // W2 chunk [D][32]
-  static constexpr int kBytes = 2 * kW13 + kW2;
-  static __device__ __forceinline__ int w13(int mat, int r, int c) {
-    return mat * kW13 + r * kRowBytes + 16 * (c ^ (swz_rows(r) & (D / 8 - 1)));
-  }
-  static __device__ __forceinline__ int w2(int rho, int a) { return 2 * kW13 + rho * 64 + 16 * (a ^ swz_64(rho)); }
+  static constexpr int kTile = kHidChunk * kRowBytes;   // one [32][D] tile
+  static constexpr int kStage = 3 * kTile;              // W1, W3, W2^T
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
   using L = ApplyLayout<D>;
   constexpr int KC = D / 32, DT = D / 16;
-  constexpr int NCH = 3 * 4 * D / 256;      // 16-byte chunks staged per thread per hidden chunk
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * L::kBytes];
+  constexpr int NPIECE = L::kStage / 1024, PPW = NPIECE / 4, kRowsPer = 1024 / L::kRowBytes;
+  constexpr int PPT = NPIECE / 3;                        // 1 KB pieces per tile
+  __shared__ __attribute__((aligned(16))) unsigned char sa[L::kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char sb[L::kStage];
 
   const int h = blockIdx.x % p.heads;
   const int64_t tile = blockIdx.x / p.heads;
@@ -59,66 +59,57 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i][0] = acc[i][1] = f32x4{0, 0, 0, 0};
 
-  const __bf16 *W1 = static_cast<const __bf16 *>(p.w1) + (int64_t)h * p.m * D;
-  const __bf16 *W3 = static_cast<const __bf16 *>(p.w3) + (int64_t)h * p.m * D;
-  const __bf16 *W2 = static_cast<const __bf16 *>(p.w2) + (int64_t)h * D * p.m;
-
-  // Staging of one hidden chunk: 12*D/8... chunks of 16 bytes, NCH per thread.
-  // Chunk e < 2*32*(D/8): W1 / W3 row r, column chunk c; else W2 row rho, chunk a.
-  u32x4 pre[NCH];
-  auto load_chunk = [&](int hc) {
+  // DMA: piece b of a stage is tile b / PPT, rows kRowsPer * (b % PPT) ..; lane l
+  // fills row r at physical chunk l % kChunks = logical chunk ^ swizzle(tile, r).
+  const char *wsrc[3] = {static_cast<const char *>(p.w1), static_cast<const char *>(p.w3),
+                         static_cast<const char *>(p.w2t)};
+  int soff[PPW];
 #pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-      const int e = tid + 256 * q;
-      const __bf16 *src;
-      if (e < 2 * kHidChunk * (D / 8)) {
-        const int mat = e / (kHidChunk * (D / 8)), rem = e % (kHidChunk * (D / 8));
-        src = (mat ? W3 : W1) + (int64_t)(hc * kHidChunk + rem / (D / 8)) * D + 8 * (rem % (D / 8));
-      } else {
-        const int f = e - 2 * kHidChunk * (D / 8);
-        src = W2 + (int64_t)(f >> 2) * p.m + hc * kHidChunk + 8 * (f & 3);
-      }
-      pre[q] = *reinterpret_cast<const u32x4 *>(src);
-    }
-  };
-  auto store_chunk = [&](int buf) {
-    unsigned char *base = smem + buf * L::kBytes;
+  for (int q = 0; q < PPW; ++q) {
+    const int piece = w * PPW + q, mat = piece / PPT;
+    const int r = kRowsPer * (piece % PPT) + l / L::kChunks;
+    const int sw = (mat < 2 ? swz_rows_b128(r) : swz_rows(r)) & (L::kChunks - 1);
+    soff[q] = (r * D + 8 * ((l % L::kChunks) ^ sw)) * 2;
+  }
+  const int64_t head_off = (int64_t)h * p.m * D * 2;
+  auto stage_chunk = [&](int hc, unsigned char *dst) {
+    const int64_t base = head_off + (int64_t)hc * kHidChunk * D * 2;   // wave-uniform
 #pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-      const int e = tid + 256 * q;
-      int off;
-      if (e < 2 * kHidChunk * (D / 8)) {
-        const int mat = e / (kHidChunk * (D / 8)), rem = e % (kHidChunk * (D / 8));
-        off = L::w13(mat, rem / (D / 8), rem % (D / 8));
-      } else {
-        const int f = e - 2 * kHidChunk * (D / 8);
-        off = L::w2(f >> 2, f & 3);
-      }
-      *reinterpret_cast<u32x4 *>(base + off) = pre[q];
+    for (int q = 0; q < PPW; ++q) {
+      const int piece = w * PPW + q;
+      copy16_to_lds(wsrc[piece / PPT] + base + soff[q], dst + piece * 1024);
     }
   };
 
-  const int nch = p.m / kHidChunk;
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int hc = 0; hc < nch; ++hc) {
-    const int cur = hc & 1;
-    const bool more = hc + 1 < nch;
-    if (more) load_chunk(hc + 1);
-    const unsigned char *base = smem + cur * L::kBytes;
+  // W1 / W3 reads: row perm_row(u, li), chunk 4kc + g  ->  base ^ 64 kc
+  int base_a[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int rw = perm_row(u, li);
+    base_a[u] = rw * L::kRowBytes + 16 * (g ^ (swz_rows_b128(rw) & (L::kChunks - 1)));
+  }
+  // W2^T transposed reads: lane supplies row 8g + 4q + li/4, column 16 dt + 4 (li % 4)
+  // and receives hidden rows 8g + 4q .. +3 of d column 16 dt + li  ->  base ^ 32 dt
+  int base_b[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 8 * g + 4 * q + (li >> 2);
+    base_b[q] = 2 * L::kTile + row * L::kRowBytes + 16 * (((li & 3) >> 1) ^ (swz_rows(row) & (L::kChunks - 1))) +
+                8 * (li & 1);
+  }
 
+  auto compute = [&](const unsigned char *base) {
     // Z^T rows = hidden perm_row(u, li) of the chunk, cols = tokens
     f32x4 z1[2][2], z3[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) z1[u][t] = z3[u][t] = f32x4{0, 0, 0, 0};
-      const int rw = perm_row(u, li);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(base + L::w13(0, rw, 4 * kc + g));
-        const bf16x8 a3 = *reinterpret_cast<const bf16x8 *>(base + L::w13(1, rw, 4 * kc + g));
+        const unsigned char *pa = base + (base_a[u] ^ (64 * kc));
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(pa);
+        const bf16x8 a3 = *reinterpret_cast<const bf16x8 *>(pa + L::kTile);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           z1[u][t] = mma(a1, qf[t][kc], z1[u][t]);
@@ -143,12 +134,28 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
     // O^T[d][tok] += W2[d][chunk] H^T
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 w2f = *reinterpret_cast<const bf16x8 *>(base + L::w2(16 * dt + li, g));
+      const bf16x8 w2f = cat8(lds_read_tr16(base + (base_b[0] ^ (32 * dt))),
+                              lds_read_tr16(base + (base_b[1] ^ (32 * dt))));
       acc[dt][0] = mma(w2f, hf[0], acc[dt][0]);
       acc[dt][1] = mma(w2f, hf[1], acc[dt][1]);
     }
-    if (more) store_chunk(cur ^ 1);
+  };
+
+  const int nch = p.m / kHidChunk;
+  stage_chunk(0, sa);
+  wait_all_memory();
+  __syncthreads();
+  for (int hc = 0; hc < nch; hc += 2) {
+    if (hc + 1 < nch) stage_chunk(hc + 1, sb);
+    compute(sa);
+    wait_all_memory();
     __syncthreads();
+    if (hc + 1 < nch) {
+      if (hc + 2 < nch) stage_chunk(hc + 2, sa);
+      compute(sb);
+      wait_all_memory();
+      __syncthreads();
+    }
   }
 
   // O[tok][16 dt + 4g + r] for r = 0..3: one 8-byte store per (dt, t)

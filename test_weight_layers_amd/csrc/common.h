@@ -93,6 +93,10 @@ __device__ __forceinline__ int perm_row(int u, int i) { return 8 * (i >> 2) + 4 
 __device__ __forceinline__ int swz_rows(int r) {
   return ((r >> 4) & 1) | ((r & 3) << 1) | (((r >> 3) & 1) << 3);
 }
+// Row-major tile with 512-byte rows read with ds_read_b128 only, 16 lanes on rows
+// perm_row(u, 0..15) at one chunk: row bits (0, 1, 3, 4) onto position bits
+// (0, 1, 2, 3) measured conflict-free on gfx950 (swz_rows is not for this pattern).
+__device__ __forceinline__ int swz_rows_b128(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
 // Tile with 64-byte rows (4 chunks, 4 rows per 256 bytes): chunk a of row r lives at
 // a ^ swz_64(r), a bijection on row bits (2, 3) within each r % 4 class, so 16 lanes
 // reading rows R..R+15 (R % 16 == 0) at one chunk hit 16 positions.

@@ -29,7 +29,8 @@ struct ApplyParams {
   void *o;
   int64_t ldo;
   const void *w1, *w3;       // [H][m][d]
-  const void *w2;            // [H][d][m]
+  const void *w2;            // [H][d][m] (general kernels)
+  const void *w2t;           // [H][m][d] transposed W2 (fast kernel)
   int64_t nq;
   int heads, m, dchunks;
 };
