@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     ap.add_argument("--no-profile-events", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time ZipMap-shaped layers at 125..2000 frames and fit t = t0 + beta*N")
     return ap.parse_args()
 
 
@@ -116,6 +118,58 @@ def cpu_baseline(cfg, frames):
                       f"{dt:.2f} s wall"}
 
 
+def linear_sweep(steps, warmup):
+    """Update (1 step) + apply on the same N tokens of the ZipMap 4x256/512 shape at
+    125..2000 frames (prefixes of one draw); least-squares fit of time against N."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
+    from test_weight_layers_amd import synth, ttt
+    from test_weight_layers_amd.configs import CONFIGS
+    frames = [125, 250, 500, 750, 1000, 2000]
+    cfg = replace(CONFIGS["c4"], frames=max(frames), extra_query=0, steps=1)
+    torch.cuda.set_device(0)
+    ttt.load()
+    full = synth.to_device(synth.make_inputs(cfg), "cuda")
+    H, d, m = cfg.heads, cfg.d, cfg.m
+    w0 = (full.w1, full.w3, full.w2)
+    rows = []
+    for f in frames:
+        n = f * cfg.tokens_per_frame
+        k, v, q, eta = full.k[:n], full.v[:n], full.q[:n], full.eta[:, :n]
+        w_out = tuple(torch.empty_like(x) for x in w0)
+        o = torch.empty((n, H * d), dtype=k.dtype, device="cuda")
+        ws_u = torch.empty(ttt.update_workspace_bytes(H, d, m, n, k.dtype), dtype=torch.uint8, device="cuda")
+        ws_a = torch.empty(ttt.apply_workspace_bytes(H, d, m, n, k.dtype), dtype=torch.uint8, device="cuda")
+
+        def step():
+            ttt.update(w0, k, v, eta, cfg.lr, 1, out=w_out, workspace=ws_u)
+            ttt.apply(w_out, q, out=o, workspace=ws_a)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        rows.append((n, (time.perf_counter() - t0) / steps))
+        print(json.dumps({"sweep_frames": f, "tokens": n, "ms": rows[-1][1] * 1e3}), flush=True)
+    ns = np.array([r[0] for r in rows], float)
+    ts = np.array([r[1] for r in rows], float)
+    A = np.stack([np.ones_like(ns), ns], 1)
+    (t0, beta), *_ = np.linalg.lstsq(A, ts, rcond=None)
+    fit = t0 + beta * ns
+    r2 = 1.0 - np.sum((ts - fit) ** 2) / np.sum((ts - ts.mean()) ** 2)
+    i1000 = frames.index(1000)
+    out = {"sweep": "zipmap-shape 4x256/512, update (1 step) + apply on the same N tokens",
+           "frames": frames, "tokens": ns.tolist(), "seconds": ts.tolist(), "t0_s": t0,
+           "beta_s_per_token": beta, "r2": r2, "max_rel_residual": float(np.max(np.abs(ts - fit) / ts)),
+           "t0_over_t_at_1000_frames": float(t0 / ts[i1000]),
+           "tokens_per_s_asymptotic": 1.0 / beta}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -125,6 +179,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        linear_sweep(args.steps, args.warmup)
         return
     from test_weight_layers_amd import synth, ttt
     from test_weight_layers_amd.configs import CONFIGS

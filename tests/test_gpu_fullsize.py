@@ -1,0 +1,151 @@
+"""GPU parity at the workloads' full sizes, in the configuration bench.py times.
+
+The fp32 CPU oracle runs the whole layer at full size (about a minute on the
+GPU machine's host cores for the 1000-frame workload); every output is compared,
+per head and per matrix, against the bf16 gate of 2e-2.  The oracle's fp32
+rounding is 1e-5-level (pinned against fp64 in test_oracle.py), far inside it.
+The streaming workload is checked on its first chunks against the oracle's
+stream, and as a whole against chunk-by-chunk GPU calls (a property at any size).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from test_weight_layers_amd import synth
+from test_weight_layers_amd.configs import CONFIGS
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from test_weight_layers_amd import ttt
+    ttt.load()
+    ttt.set_option(ttt.OPT_FORCE_GENERAL, 0)
+    ttt.set_option(ttt.OPT_SPLITS, 0)
+
+
+def _f32(t):
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _rel_rows(gpu_o, ref_o, cols, block=131072):
+    """Relative Frobenius error of columns `cols` of two [rows, width] arrays, in row blocks."""
+    num = den = 0.0
+    for r0 in range(0, ref_o.shape[0], block):
+        a = gpu_o[r0:r0 + block, cols].double().cpu().numpy()
+        b = ref_o[r0:r0 + block, cols].astype(np.float64)
+        num += float(np.sum((a - b) ** 2))
+        den += float(np.sum(b ** 2))
+    return (num / den) ** 0.5
+
+
+def _gpu_layer(cfg, inp):
+    from test_weight_layers_amd import ttt
+    d = synth.to_device(inp, "cuda")
+    H, dd, m = cfg.heads, cfg.d, cfg.m
+    v = d.v
+    if cfg.conv:
+        v = ttt.shortconv2d(d.v, d.wconv, cfg.frames, cfg.tokens_per_frame, cfg.n_special, cfg.grid_h,
+                            cfg.grid_w)
+    g = torch.empty(3 * H * m * dd, device="cuda")
+    ns = torch.empty_like(g)
+    w_hat = ttt.update((d.w1, d.w3, d.w2), d.k, v, d.eta, cfg.lr, cfg.steps, grad_out=g, ns_out=ns)
+    o = ttt.apply(w_hat, d.q)
+    # determinism and composition: the same call again, and one step at a time
+    w_again = ttt.update((d.w1, d.w3, d.w2), d.k, v, d.eta, cfg.lr, cfg.steps)
+    w_step = (d.w1, d.w3, d.w2)
+    for _ in range(cfg.steps):
+        w_step = ttt.update(w_step, d.k, v, d.eta, cfg.lr, 1)
+    torch.cuda.synchronize()
+    for a, b, c in zip(w_hat, w_again, w_step):
+        assert torch.equal(a, b) and torch.equal(a, c)
+    del d, v, w_again, w_step
+    mat = H * m * dd
+    split = lambda t: (t[:mat].view(H, m, dd).cpu().numpy(), t[mat:2 * mat].view(H, m, dd).cpu().numpy(),
+                       t[2 * mat:].view(H, dd, m).cpu().numpy())
+    return o, tuple(x.cpu().numpy() for x in w_hat), split(g), split(ns)
+
+
+def _oracle_layer(cfg, inp):
+    conv = None
+    if cfg.conv:
+        conv = dict(wconv=_f32(inp.wconv), frames=cfg.frames, tokens_per_frame=cfg.tokens_per_frame,
+                    n_special=cfg.n_special, grid_h=cfg.grid_h, grid_w=cfg.grid_w)
+    return oracle.layer(_f32(inp.w1), _f32(inp.w3), _f32(inp.w2), _f32(inp.k), _f32(inp.v), _f32(inp.eta),
+                        _f32(inp.q), cfg.lr, cfg.steps, conv=conv)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c5a", "c4", "c3", "c2"])
+def test_full_size_layer(name):
+    cfg = CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    print(f"{cfg.name}: N={inp.k.shape[0]} Nq={inp.q.shape[0]} H={cfg.heads} d={cfg.d} m={cfg.m} "
+          f"steps={cfg.steps} conv={cfg.conv}", flush=True)
+    o_gpu, w_gpu, g_gpu, ns_gpu = _gpu_layer(cfg, inp)
+    o_ref, w_ref, g_ref, ns_ref = _oracle_layer(cfg, inp)
+    w0 = [_f32(t) for t in (inp.w1, inp.w3, inp.w2)]
+    worst = {}
+    for h in range(cfg.heads):
+        for j, nm in enumerate(("1", "3", "2")):
+            worst[f"G{nm}[h{h}]"] = _rel(g_gpu[j][h], g_ref[j][h])
+            worst[f"NS{nm}[h{h}]"] = _rel(ns_gpu[j][h], ns_ref[j][h])
+            worst[f"W{nm}[h{h}]"] = _rel(w_gpu[j][h], w_ref[j][h])
+            worst[f"dW{nm}[h{h}]"] = _rel(w_gpu[j][h] - w0[j][h], w_ref[j][h] - w0[j][h])
+        c = slice(h * cfg.d, (h + 1) * cfg.d)
+        worst[f"O[h{h}]"] = _rel_rows(o_gpu, o_ref, c)
+    top = max(worst, key=worst.get)
+    print(f"{cfg.name}: worst {top} = {worst[top]:.3e}", flush=True)
+    bad = {k: v for k, v in worst.items() if not v <= TOL}
+    assert not bad, bad
+
+
+@pytest.mark.timeout(600)
+def test_stream_first_chunks_and_whole_stream_property():
+    from test_weight_layers_amd import ttt
+    cfg = CONFIGS["c5b"]
+    chunk = cfg.chunk_frames * cfg.tokens_per_frame
+    n_check = 6 * chunk
+    inp = synth.make_inputs(cfg)                      # the full 4000-frame stream
+    d = synth.to_device(inp, "cuda")
+    H = cfg.heads
+    w_full = tuple(x.clone() for x in (d.w1, d.w3, d.w2))
+    o_full = ttt.stream(w_full, d.k, d.v, d.eta, d.q, cfg.lr, 1, chunk)
+    # whole stream == explicit chunk-by-chunk apply/update calls
+    w_seq = tuple(x.clone() for x in (d.w1, d.w3, d.w2))
+    o_seq = torch.empty_like(o_full)
+    for t0 in range(0, inp.k.shape[0], chunk):
+        t1 = min(inp.k.shape[0], t0 + chunk)
+        ttt.apply(w_seq, d.q[t0:t1], out=o_seq[t0:t1])
+        ttt.update(w_seq, d.k[t0:t1], d.v[t0:t1], d.eta[:, t0:t1], cfg.lr, 1, out=w_seq)
+    torch.cuda.synchronize()
+    assert torch.equal(o_full, o_seq)
+    for a, b in zip(w_full, w_seq):
+        assert torch.equal(a, b)
+    # first chunks against the oracle's stream
+    w_part = tuple(x.clone() for x in (d.w1, d.w3, d.w2))
+    o_part = ttt.stream(w_part, d.k[:n_check], d.v[:n_check], d.eta[:, :n_check], d.q[:n_check], cfg.lr, 1,
+                        chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o_part, o_full[:n_check])
+    o_ref, w_ref = oracle.stream(_f32(inp.w1), _f32(inp.w3), _f32(inp.w2), _f32(inp.k[:n_check]),
+                                 _f32(inp.v[:n_check]), _f32(inp.eta[:, :n_check]), _f32(inp.q[:n_check]),
+                                 cfg.lr, 1, chunk)
+    w0 = [_f32(t) for t in (inp.w1, inp.w3, inp.w2)]
+    for h in range(H):
+        c = slice(h * cfg.d, (h + 1) * cfg.d)
+        assert _rel(o_part[:, c].double().cpu().numpy(), o_ref[:, c]) <= TOL
+        for j in range(3):
+            got = w_part[j][h].cpu().numpy() - w0[j][h]
+            assert _rel(got, w_ref[j][h] - w0[j][h]) <= TOL
