@@ -164,8 +164,13 @@ int ttt_stream(int32_t heads, int32_t d, int32_t m,
  *     results agree within the bf16 tolerance.  Default 0.
  *   TTT_OPT_SPLITS: value > 0 fixes the number of token ranges the gradient is
  *     split into (0 = automatic, sized to fill the GPU).  Affects workspace size.
+ *   TTT_OPT_NS_UNFUSED: value != 0 runs the split-K reduction, the Frobenius
+ *     normalisation, each Newton-Schulz product, the weight step and the operand
+ *     casts as separate kernels, instead of folding the normalisation, the step
+ *     and the casts into the product kernels.  Same mathematics, different fp32
+ *     rounding order; default 0 (folded).
  */
-typedef enum { TTT_OPT_FORCE_GENERAL = 0, TTT_OPT_SPLITS = 1 } ttt_option;
+typedef enum { TTT_OPT_FORCE_GENERAL = 0, TTT_OPT_SPLITS = 1, TTT_OPT_NS_UNFUSED = 2 } ttt_option;
 int ttt_set_option(int32_t option, int64_t value);
 
 /*

@@ -31,6 +31,7 @@ int fail(int status, const char *fmt, ...) {
 // ----------------------------------------------------------------- options
 int64_t g_force_general = 0;   // 1: use the general kernels even where a fast one exists
 int64_t g_splits = 0;          // >0: fixed number of token splits for the gradient
+int64_t g_ns_unfused = 0;      // 1: normalisation, step and casts as kernels of their own
 
 // ----------------------------------------------------------------- timing
 struct Pending {
@@ -108,7 +109,7 @@ struct UpdatePlan {
   bool bf16, fast, xcd;
   int dchunks, splits, grid;
   int64_t n, nblk;
-  size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_a, off_b, total;
+  size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_xt0, off_xt1, off_a, off_b, total;
 };
 
 UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
@@ -144,6 +145,10 @@ UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
   off = align256(off + 3 * mat * 4);
   p.off_x1 = off;
   off = align256(off + 3 * mat * 4);
+  p.off_xt0 = off;
+  off = align256(off + 3 * mat * 4);
+  p.off_xt1 = off;
+  off = align256(off + 3 * mat * 4);
   p.off_a = off;
   off = align256(off + (size_t)3 * H * p.r * p.r * 4);
   p.off_b = off;
@@ -168,8 +173,13 @@ constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
 constexpr int kNsIters = 5;
 constexpr float kNsEps = 1e-7f;
 
+// ops_ready: the operand copies of `in` are already at the start of the workspace
+// (written by the previous call's last step or by an apply cast of the same layout).
+// keep_ops: the last step leaves the operand copies of `out` there.
 int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v, int64_t ld, const float *eta,
-              int64_t eta_hs, float lr, int steps, float *grad_out, float *ns_out, char *ws, hipStream_t s) {
+              int64_t eta_hs, float lr, int steps, float *grad_out, float *ns_out, char *ws, hipStream_t s,
+              bool ops_ready = false, bool keep_ops = false) {
+  const bool fused = !g_ns_unfused;
   const size_t mat = (size_t)P.H * P.d * P.m;
   void *wop = ws + P.off_wop;
   float *part = reinterpret_cast<float *>(ws + P.off_part);
@@ -186,25 +196,54 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
     const bool last = t == steps - 1;
     GradParams gp{};
     gp.k = k, gp.v = v, gp.ld = ld, gp.eta = eta, gp.eta_hs = eta_hs;
+    const bool need_cast = t == 0 ? !ops_ready : !fused;    // the folded step writes the next copies
     if (P.bf16) {
       __bf16 *b = static_cast<__bf16 *>(wop);
-      st = run(TTT_K_CAST, "cast", s, [&] {
-        return launch_cast(src.w1, src.w3, src.w2, b, b + mat, b + 2 * mat, nullptr, P.H, P.d, P.m, true, s);
-      });
-      if (st) return st;
+      if (need_cast) {
+        st = run(TTT_K_CAST, "cast", s, [&] {
+          return launch_cast(src.w1, src.w3, src.w2, b, b + mat, b + 2 * mat, nullptr, P.H, P.d, P.m, true, s);
+        });
+        if (st) return st;
+      }
       gp.w1 = b, gp.w3 = b + mat, gp.w2t = b + 2 * mat;
     } else {
       float *w2t = static_cast<float *>(wop);
-      st = run(TTT_K_CAST, "cast", s, [&] {
-        return launch_cast(src.w1, src.w3, src.w2, nullptr, nullptr, w2t, nullptr, P.H, P.d, P.m, false, s);
-      });
-      if (st) return st;
+      if (need_cast) {
+        st = run(TTT_K_CAST, "cast", s, [&] {
+          return launch_cast(src.w1, src.w3, src.w2, nullptr, nullptr, w2t, nullptr, P.H, P.d, P.m, false, s);
+        });
+        if (st) return st;
+      }
       gp.w1 = src.w1, gp.w3 = src.w3, gp.w2t = w2t;
     }
     gp.part = part, gp.n = P.n, gp.nblk = P.nblk;
     gp.heads = P.H, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
     st = run(TTT_K_GRAD, "gradient", s, [&] { return launch_grad(gp, P.d, P.bf16, P.fast, P.grid, s); });
     if (st) return st;
+    if (fused) {
+      NsStepParams np{};
+      np.part = part, np.splits = P.splits, np.per_split = (int64_t)3 * mat;
+      np.grad_out = last ? grad_out : nullptr, np.ns_out = last ? ns_out : nullptr;
+      np.sumsq = sumsq;
+      np.x[0] = x0, np.x[1] = x1;
+      np.xt[0] = reinterpret_cast<float *>(ws + P.off_xt0), np.xt[1] = reinterpret_cast<float *>(ws + P.off_xt1);
+      np.am = am, np.bm = bm;
+      np.w1 = src.w1, np.w3 = src.w3, np.w2 = src.w2;
+      np.w1o = out.w1, np.w3o = out.w3, np.w2o = out.w2;
+      if (!last || keep_ops) {
+        if (P.bf16) {
+          __bf16 *b = static_cast<__bf16 *>(wop);
+          np.op1v = b, np.op3v = b + mat, np.op2tv = b + 2 * mat;
+        } else {
+          np.op2tv = wop;
+        }
+      }
+      np.lr = lr, np.eps = kNsEps, np.a_coef = kNsA, np.b_coef = kNsB, np.c_coef = kNsC;
+      np.iters = kNsIters, np.heads = P.H, np.d = P.d, np.m = P.m, np.r = P.r, np.c = P.c;
+      st = run(TTT_K_NS, "newton_schulz", s, [&] { return launch_ns_optimiser(np, P.bf16, s); });
+      if (st) return st;
+      continue;
+    }
     st = run(TTT_K_REDUCE, "reduce", s, [&] {
       return launch_reduce(part, P.splits, (int64_t)3 * mat, g, last ? grad_out : nullptr, sumsq, s);
     });
@@ -236,8 +275,14 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
   return TTT_OK;
 }
 
+// The workspace starts with the operand copies in the update's layout when the
+// fast bf16 kernel runs (W1, W3, W2^T as [H][m][d]); ops_ready skips their cast.
+bool apply_shares_update_ops(int d, int dtype) {
+  return dtype == TTT_BF16 && !g_force_general && apply_fast_supported(d, true);
+}
+
 int do_apply(int H, int d, int m, W3 w, const void *q, int64_t ldq, void *o, int64_t ldo, int64_t nq, int dtype,
-             char *ws, hipStream_t s) {
+             char *ws, hipStream_t s, bool ops_ready = false) {
   if (nq == 0) return TTT_OK;
   const bool bf16 = dtype == TTT_BF16;
   const bool fast = !g_force_general && apply_fast_supported(d, bf16);
@@ -248,11 +293,13 @@ int do_apply(int H, int d, int m, W3 w, const void *q, int64_t ldq, void *o, int
     // the fast kernel reads W2 transposed ([H][m][d]), the general one as stored
     const size_t mat = (size_t)H * d * m;
     __bf16 *b = reinterpret_cast<__bf16 *>(ws);
-    const int st = run(TTT_K_CAST, "cast", s, [&] {
-      return launch_cast(w.w1, w.w3, w.w2, b, b + mat, fast ? b + 2 * mat : nullptr, fast ? nullptr : b + 2 * mat, H,
-                         d, m, true, s);
-    });
-    if (st) return st;
+    if (!(ops_ready && fast)) {
+      const int st = run(TTT_K_CAST, "cast", s, [&] {
+        return launch_cast(w.w1, w.w3, w.w2, b, b + mat, fast ? b + 2 * mat : nullptr, fast ? nullptr : b + 2 * mat,
+                           H, d, m, true, s);
+      });
+      if (st) return st;
+    }
     ap.w1 = b, ap.w3 = b + mat, ap.w2 = b + 2 * mat, ap.w2t = b + 2 * mat;
   } else {
     ap.w1 = w.w1, ap.w3 = w.w3, ap.w2 = w.w2;
@@ -400,15 +447,24 @@ int ttt_stream(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   const size_t es = esize(dtype);
+  // With the folded optimiser step, each chunk's last step leaves the operand copies
+  // of the new weights at the start of the workspace, where the next chunk's apply
+  // (when its layout is the same) and gradient read them: one cast per stream.
+  const bool carry = !g_ns_unfused;
+  const bool shared = carry && apply_shares_update_ops(d, dtype);
   for (int64_t t0 = 0; t0 < n; t0 += chunk) {
     const int64_t len = n - t0 < chunk ? n - t0 : chunk;
+    const bool first = t0 == 0;
     st = do_apply(heads, d, m, W3{w1, w3, w2}, static_cast<const char *>(q) + t0 * ld_q * es, ld_q,
-                  static_cast<char *>(o) + t0 * ld_o * es, ld_o, len, dtype, ws, s);
+                  static_cast<char *>(o) + t0 * ld_o * es, ld_o, len, dtype, ws, s, shared && !first);
     if (st) return st;
     const UpdatePlan P = plan_update(heads, d, m, len, dtype);
+    // the apply just cast W into the update's operand layout (shared), or the previous
+    // chunk's step left them (fp32 keeps only W2^T there, which apply never touches)
+    const bool ready = shared || (carry && dtype == TTT_F32 && !first);
     st = do_update(P, W3{w1, w3, w2}, W3o{w1, w3, w2}, static_cast<const char *>(k) + t0 * ld_kv * es,
                    static_cast<const char *>(v) + t0 * ld_kv * es, ld_kv, eta + t0, eta_head_stride, lr, steps,
-                   nullptr, nullptr, ws, s);
+                   nullptr, nullptr, ws, s, ready, carry);
     if (st) return st;
   }
   return TTT_OK;
@@ -421,6 +477,7 @@ int ttt_set_option(int32_t option, int64_t value) {
       if (value < 0) return fail(TTT_EINVAL, "splits must be >= 0");
       g_splits = value;
       return TTT_OK;
+    case TTT_OPT_NS_UNFUSED: g_ns_unfused = value != 0; return TTT_OK;
   }
   return fail(TTT_EINVAL, "unknown option %d", option);
 }

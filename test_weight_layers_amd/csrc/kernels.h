@@ -75,6 +75,27 @@ hipError_t launch_ns_step(const float *x, const float *w1, const float *w3, cons
                           float *w3o, float *w2o, float *ns_out, float lr, const NsShape &sh,
                           hipStream_t s);
 
+// The optimiser step in 1 + 3*iters launches: reduce the split partials,
+// Newton-Schulz with the Frobenius scale folded in, and W_out = W - lr * NS(G).
+// Writes grad_out / ns_out ([3][H] matrices in G's layout) when non-null and the
+// operand copies op1, op3 ([H][m][d]) and op2t (W2^T, [H][m][d]) when non-null
+// (element type: bf16 when the launcher's bf16 flag is set, else fp32).
+struct NsStepParams {
+  const float *part;         // [splits][3][H][m*d]
+  int splits;
+  int64_t per_split;         // 3*H*m*d
+  float *grad_out, *ns_out;
+  float *sumsq;              // [3H][(m/64)(d/64)] tile sums of squares
+  float *x[2], *xt[2];       // [3H][r][c] iterates and their transposes [3H][c][r]
+  float *am, *bm;            // [3H][r][r]
+  const float *w1, *w3, *w2;
+  float *w1o, *w3o, *w2o;
+  void *op1v, *op3v, *op2tv;
+  float lr, eps, a_coef, b_coef, c_coef;
+  int iters, heads, d, m, r, c;
+};
+hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s);
+
 hipError_t launch_conv(const void *v, void *out, int64_t ld, const float *w, int frames, int tpf,
                        int nsp, int gh, int gw, int channels, bool bf16, hipStream_t s);
 

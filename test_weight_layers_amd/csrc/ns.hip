@@ -180,7 +180,242 @@ hipError_t cast_impl(const float *w1, const float *w3, const float *w2, void *w1
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- optimiser step
+// The optimiser step as 16 launches: a preparation kernel (split-K sum of the
+// gradient partials in fixed order, G and G^T copies, per-tile sums of squares)
+// and one tile kernel per Newton-Schulz product.  The scale s = 1 / (||G|| + eps)
+// is folded into the first iteration's coefficients (A = s^2 G G^T,
+// X' = a s G + B (s G)), and the last product's epilogue writes W_out, the
+// optional NS copy and the operand copies that the next gradient pass and the
+// apply kernel read, so neither a normalisation nor a step nor a cast kernel runs.
+//
+// Every product is an "NT" product C[i][j] = sum_k P[i][k] Q[j][k] of row panels:
+//   A = X X^T           (P = Q = X,  K = c)
+//   A A                 (P = Q = A,  K = r; A is symmetric)
+//   B X                 (P = B, Q = X^T, K = r; X^T is kept alongside X)
+// on 64x64 output tiles, 4 waves of 32x32, K staged through LDS 32 at a time
+// with the next chunk's loads in flight.
+
+constexpr int kT = 64;        // output tile
+constexpr int kKc = 32;       // K chunk
+constexpr int kLdsW = kKc + 4;
+
+struct NsSmem {
+  union {
+    struct {
+      float a[2][kT][kLdsW];
+      float b[2][kT][kLdsW];
+    } g;
+    float tr[kT][kT + 1];
+  };
+  float red[256];
+};
+
+// acc (per wave: 2x2 blocks of 16x16) = P[0 .. 63][0..K) Q[0 .. 63][0..K)^T
+__device__ __forceinline__ void tile_nt(const float *__restrict__ P, int ldp, const float *__restrict__ Q, int ldq,
+                                        int K, NsSmem &sm, f32x4 acc[2][2]) {
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
+  const int lr = t >> 3, lc = (t & 7) * 4;          // loader: rows lr, lr + 32; 4 floats at lc
+#pragma unroll
+  for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x4{0, 0, 0, 0};
+  f32x4 pa[2], pb[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 32 * u) * ldp + lc);
+    pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 32 * u) * ldq + lc);
+  }
+  const int nk = K / kKc;
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<f32x4 *>(&sm.g.a[buf][lr + 32 * u][lc]) = pa[u];
+      *reinterpret_cast<f32x4 *>(&sm.g.b[buf][lr + 32 * u][lc]) = pb[u];
+    }
+    __syncthreads();
+    if (kc + 1 < nk) {
+      const int k0 = (kc + 1) * kKc;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 32 * u) * ldp + k0 + lc);
+        pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 32 * u) * ldq + k0 + lc);
+      }
+    }
+    const int ra = (w >> 1) * 32 + li, rb = (w & 1) * 32 + li;
+    const f32x8 a0 = ld8(&sm.g.a[buf][ra][8 * g]), a1 = ld8(&sm.g.a[buf][ra + 16][8 * g]);
+    const f32x8 b0 = ld8(&sm.g.b[buf][rb][8 * g]), b1 = ld8(&sm.g.b[buf][rb + 16][8 * g]);
+    acc[0][0] = mma(a0, b0, acc[0][0]);
+    acc[0][1] = mma(a0, b1, acc[0][1]);
+    acc[1][0] = mma(a1, b0, acc[1][0]);
+    acc[1][1] = mma(a1, b1, acc[1][1]);
+  }
+}
+
+// Deterministic block sum (every workgroup computes the same value the same way).
+__device__ __forceinline__ float block_sum(float v, NsSmem &sm) {
+  sm.red[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) sm.red[threadIdx.x] += sm.red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float r = sm.red[0];
+  __syncthreads();
+  return r;
+}
+
+// s_b = 1 / (||G_b||_F + eps) from the tile sums of squares, the same in every workgroup
+__device__ __forceinline__ float ns_scale(const NsStepParams &p, int b, NsSmem &sm) {
+  const int tiles_g = (p.m / kT) * (p.d / kT);
+  float v = 0.0f;
+  for (int i = threadIdx.x; i < tiles_g; i += 256) v += p.sumsq[(int64_t)b * tiles_g + i];
+  return 1.0f / (sqrtf(block_sum(v, sm)) + p.eps);
+}
+
+// Launch-order block id -> work item, so that consecutive items (tiles of one
+// matrix, which read the same panels) run on one XCD (blocks go round-robin
+// over the 8 XCDs).
+__device__ __forceinline__ int xcd_item() {
+  const int n = gridDim.x, b = blockIdx.x;
+  return n % 8 == 0 ? (b & 7) * (n >> 3) + (b >> 3) : b;
+}
+
+__global__ __launch_bounds__(256) void ns_prep_kernel(NsStepParams p) {
+  __shared__ NsSmem sm;
+  const int H = p.heads, d = p.d, m = p.m;
+  const int64_t mat = (int64_t)d * m;
+  const int t = threadIdx.x;
+  const int tiles_g = (m / kT) * (d / kT);
+  const int tile = xcd_item();
+  const int b = tile / tiles_g, tt = tile % tiles_g;
+  const int j = b / H;
+  const int rows = j < 2 ? m : d, cols = j < 2 ? d : m;    // G_b is [rows][cols]
+  const int ct = cols / kT;
+  const int r0 = (tt / ct) * kT, c0 = (tt % ct) * kT;
+  const bool tr = rows > cols;                             // X_b = G_b^T
+  float *gl = (tr ? p.xt[0] : p.x[0]) + (int64_t)b * mat;  // buffer in G's layout
+  float *gt = (tr ? p.x[0] : p.xt[0]) + (int64_t)b * mat;  // buffer in G^T's layout
+  float ss = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = t + 256 * u, rr = q >> 4, cc = (q & 15) * 4;
+    const int64_t e = (int64_t)b * mat + (int64_t)(r0 + rr) * cols + c0 + cc;
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(p.part + e);
+    for (int s = 1; s < p.splits; ++s) acc += *reinterpret_cast<const f32x4 *>(p.part + (int64_t)s * p.per_split + e);
+    if (p.grad_out) *reinterpret_cast<f32x4 *>(p.grad_out + e) = acc;
+    *reinterpret_cast<f32x4 *>(gl + (int64_t)(r0 + rr) * cols + c0 + cc) = acc;
+#pragma unroll
+    for (int z = 0; z < 4; ++z) sm.tr[rr][cc + z] = acc[z];
+    ss += acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {        // G^T tile: row c0 + rr, columns r0 + cc ..
+    const int q = t + 256 * u, rr = q >> 4, cc = (q & 15) * 4;
+    const f32x4 v{sm.tr[cc][rr], sm.tr[cc + 1][rr], sm.tr[cc + 2][rr], sm.tr[cc + 3][rr]};
+    *reinterpret_cast<f32x4 *>(gt + (int64_t)(c0 + rr) * rows + r0 + cc) = v;
+  }
+  const float tot = block_sum(ss, sm);
+  if (t == 0) p.sumsq[tile] = tot;
+}
+
+// PH 0: A = X X^T; 1: B = b A + c A A; 2: X' = a X + B X; 3: the last X' as the step.
+template <typename T, int PH>
+__global__ __launch_bounds__(256) void ns_tile_kernel(NsStepParams p, int cur, int first) {
+  __shared__ NsSmem sm;
+  const int H = p.heads, d = p.d, m = p.m, r = p.r, c = p.c;
+  const int64_t mat = (int64_t)d * m, srr = (int64_t)r * r;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
+  const int rt = r / kT, nt = PH < 2 ? rt : c / kT;        // output tiles per matrix: rt x nt
+  const int tile = xcd_item();
+  const int b = tile / (rt * nt), ti = (tile / nt) % rt, tj = tile % nt;
+  const float *X = p.x[cur] + (int64_t)b * mat, *XT = p.xt[cur] + (int64_t)b * mat;
+  const float *A = p.am + b * srr;
+  float *Bm = p.bm + b * srr;
+  float alpha = 1.0f;
+  if (first && (PH == 0 || PH >= 2)) {
+    const float s = ns_scale(p, b, sm);
+    alpha = PH == 0 ? s * s : s;
+  }
+  f32x4 acc[2][2];
+  if (PH == 0) tile_nt(X + (int64_t)ti * kT * c, c, X + (int64_t)tj * kT * c, c, c, sm, acc);
+  if (PH == 1) tile_nt(A + (int64_t)ti * kT * r, r, A + (int64_t)tj * kT * r, r, r, sm, acc);
+  if (PH >= 2) tile_nt(Bm + (int64_t)ti * kT * r, r, XT + (int64_t)tj * kT * r, r, r, sm, acc);
+  const int hj = b / H, h = b % H;
+  const bool tr = (hj < 2 ? m : d) > (hj < 2 ? d : m);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = ti * kT + (w >> 1) * 32 + 16 * a + 4 * g, jj = tj * kT + (w & 1) * 32 + 16 * e + li;
+      if (PH == 0) {
+#pragma unroll
+        for (int z = 0; z < 4; ++z) p.am[b * srr + (int64_t)(i + z) * r + jj] = alpha * acc[a][e][z];
+      } else if (PH == 1) {
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          const int64_t o = (int64_t)(i + z) * r + jj;
+          Bm[o] = p.c_coef * acc[a][e][z] + p.b_coef * A[o];
+        }
+      } else {
+        // X[i .. i+3][jj] is the contiguous X^T[jj][i .. i+3]
+        const f32x4 xo = *reinterpret_cast<const f32x4 *>(XT + (int64_t)jj * r + i);
+        const float beta = p.a_coef * alpha;
+        f32x4 v;
+#pragma unroll
+        for (int z = 0; z < 4; ++z) v[z] = alpha * acc[a][e][z] + beta * xo[z];
+        if (PH == 2) {
+          float *Xo = p.x[cur ^ 1] + (int64_t)b * mat;
+#pragma unroll
+          for (int z = 0; z < 4; ++z) Xo[(int64_t)(i + z) * c + jj] = v[z];
+          *reinterpret_cast<f32x4 *>(p.xt[cur ^ 1] + (int64_t)b * mat + (int64_t)jj * r + i) = v;
+        } else {
+          // X_b[i][jj] is NS(G_b) at (i, jj), or at (jj, i) when X_b = G_b^T
+          const float *W = hj == 0 ? p.w1 : (hj == 1 ? p.w3 : p.w2);
+          float *Wo = hj == 0 ? p.w1o : (hj == 1 ? p.w3o : p.w2o);
+          const int gcols = hj < 2 ? d : m;
+          T *op = static_cast<T *>(hj == 0 ? p.op1v : (hj == 1 ? p.op3v : p.op2tv));
+#pragma unroll
+          for (int z = 0; z < 4; ++z) {
+            const int gr = tr ? jj : i + z, gc = tr ? i + z : jj;
+            const int64_t ew = (int64_t)h * mat + (int64_t)gr * gcols + gc;
+            const float nw = W[ew] - p.lr * v[z];
+            Wo[ew] = nw;
+            if (p.ns_out) p.ns_out[(int64_t)b * mat + (int64_t)gr * gcols + gc] = v[z];
+            if (op) {
+              // W1/W3 copies keep G's [m][d] layout; W2 [d][m] is copied transposed
+              const int64_t oe = hj < 2 ? ew : (int64_t)h * mat + (int64_t)gc * d + gr;
+              op[oe] = from_f32<T>(nw);
+            }
+          }
+        }
+      }
+    }
+}
+
+template <typename T>
+hipError_t ns_optimiser_impl(const NsStepParams &p, hipStream_t s) {
+  const int B = 3 * p.heads, rt = p.r / kT, ct = p.c / kT;
+  hipLaunchKernelGGL(ns_prep_kernel, dim3(B * rt * ct), dim3(256), 0, s, p);
+  int cur = 0;
+  for (int it = 0; it < p.iters; ++it) {
+    const int first = it == 0;
+    hipLaunchKernelGGL((ns_tile_kernel<T, 0>), dim3(B * rt * rt), dim3(256), 0, s, p, cur, first);
+    hipLaunchKernelGGL((ns_tile_kernel<T, 1>), dim3(B * rt * rt), dim3(256), 0, s, p, cur, first);
+    if (it + 1 < p.iters)
+      hipLaunchKernelGGL((ns_tile_kernel<T, 2>), dim3(B * rt * ct), dim3(256), 0, s, p, cur, first);
+    else
+      hipLaunchKernelGGL((ns_tile_kernel<T, 3>), dim3(B * rt * ct), dim3(256), 0, s, p, cur, first);
+    cur ^= 1;
+  }
+  return hipGetLastError();
+}
 }  // namespace
+
+hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s) {
+  return bf16 ? ns_optimiser_impl<__bf16>(p, s) : ns_optimiser_impl<float>(p, s);
+}
 
 hipError_t launch_cast(const float *w1, const float *w3, const float *w2, void *w1o, void *w3o, void *w2to,
                        void *w2o, int heads, int d, int m, bool bf16, hipStream_t s) {

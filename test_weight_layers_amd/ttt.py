@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libttt.so")
 
 TTT_F32, TTT_BF16 = 0, 1
-OPT_FORCE_GENERAL, OPT_SPLITS = 0, 1
+OPT_FORCE_GENERAL, OPT_SPLITS, OPT_NS_UNFUSED = 0, 1, 2
 KERNEL_KINDS = ("conv", "cast", "grad", "reduce", "ns", "apply")
 EXPORTS = ("ttt_last_error", "ttt_update_workspace_bytes", "ttt_apply_workspace_bytes", "ttt_update",
            "ttt_apply", "ttt_shortconv2d", "ttt_stream_workspace_bytes", "ttt_stream", "ttt_set_option",
