@@ -88,6 +88,9 @@ int ttt_apply_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t nq,
  * k, v            : [n][ld_kv] keys and (already conv-mixed) values, `dtype`.
  * eta             : per-token rates, see conventions.
  * n               : tokens (>= 0; n = 0 gives G = 0, NS(G) = 0, W unchanged).
+ *                   At most 2^31 - 65 per call, and 32 rows of ld_kv must span
+ *                   < 2 GiB (TTT_EUNSUPPORTED otherwise; ttt_stream applies the
+ *                   limit per chunk).
  * lr              : step size (lr = 0 leaves W bit-identical).
  * steps           : inner steps, >= 1.
  * grad_out, ns_out: optional (NULL to skip), 3*H*m*d floats each, device:

@@ -96,6 +96,17 @@ int check_rows(const void *p, int64_t ld, int heads, int d, int dtype, const cha
   return TTT_OK;
 }
 
+// The gradient kernels index tokens and the rows of one 32-token block with 32-bit
+// integers: n must leave room for a whole block, and 32 rows must span < 2 GiB.
+constexpr int64_t kMaxTokens = 2147483647LL - 64;
+int check_token_limits(int64_t n, int64_t ld, int dtype, const char *name) {
+  if (n > kMaxTokens) return fail(TTT_EUNSUPPORTED, "n=%lld exceeds %lld tokens per call", (long long)n,
+                                  (long long)kMaxTokens);
+  if (n > 0 && ld * (int64_t)esize(dtype) * 32 >= 2147483648LL)
+    return fail(TTT_EUNSUPPORTED, "row stride of %s too large (32 rows must span < 2 GiB)", name);
+  return TTT_OK;
+}
+
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
   return x < y + nb && y < x + na;
@@ -372,6 +383,7 @@ int ttt_update(int32_t heads, int32_t d, int32_t m, const float *w1, const float
   if (n < 0) return fail(TTT_EINVAL, "n must be >= 0");
   if (steps < 1) return fail(TTT_EINVAL, "steps must be >= 1");
   if (!std::isfinite(lr)) return fail(TTT_EINVAL, "lr must be finite");
+  if ((st = check_token_limits(n, ld_kv, dtype, "k/v"))) return st;
   if (n > 0) {
     if ((st = check_rows(k, ld_kv, heads, d, dtype, "k"))) return st;
     if ((st = check_rows(v, ld_kv, heads, d, dtype, "v"))) return st;
@@ -436,6 +448,7 @@ int ttt_stream(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float 
   if (n < 0 || chunk < 1 || steps < 1) return fail(TTT_EINVAL, "need n >= 0, chunk >= 1, steps >= 1");
   if (!std::isfinite(lr)) return fail(TTT_EINVAL, "lr must be finite");
   if (n == 0) return TTT_OK;
+  if ((st = check_token_limits(chunk < n ? chunk : n, ld_kv, dtype, "k/v"))) return st;
   if ((st = check_rows(k, ld_kv, heads, d, dtype, "k"))) return st;
   if ((st = check_rows(v, ld_kv, heads, d, dtype, "v"))) return st;
   if ((st = check_rows(q, ld_q, heads, d, dtype, "q"))) return st;

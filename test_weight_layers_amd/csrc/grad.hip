@@ -19,6 +19,8 @@
 // feeds dZ1, dZ3, H' straight back into the MFMA as operands: the tokens'
 // row order is permuted (perm_row) so that the accumulator layout of the first
 // product is the operand layout of the second, with no LDS round trip.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -26,31 +28,37 @@ namespace ttt {
 namespace {
 
 // ---------------------------------------------------------------- fast path
-// bf16 tokens, D <= 256.  Each 32-token block of K and V is DMA'd into LDS once,
-// row-major and swizzled, into one of three stages.  The d-reductions read it as
-// MFMA fragments with ds_read_b128; the token reductions read the same tile
-// transposed with ds_read_b64_tr_b16.  Each wave keeps its 16 rows of W1, W3 and
-// W2^T in registers.
-//
-// Software pipeline over blocks: iteration i runs the d-reductions of block i,
-// then the SwiGLU backward of block i (VALU) interleaved with the token
-// contractions of block i-1 (MFMA), while block i+1 streams into the third stage.
+// bf16 tokens, D <= 256.  A workgroup has 8 waves in two roles that share the SIMDs
+// (wave w and wave w + 4 run on one SIMD), so the hardware interleaves them:
+//   waves 0-3 ("forward"): z1, z3, p of a block for 16 hidden units each (MFMA,
+//     weights in registers, K/V fragments from LDS), then the SwiGLU backward (VALU);
+//     the packed bf16 operands dZ1, dZ3, H' go to LDS;
+//   waves 4-7 ("contraction"): the token contractions of the previous block for
+//     the same hidden units, fp32 accumulators G1, G3, G2 in registers.
+// K and V of a block are DMA'd into LDS once (row-major, swizzled) into one of three
+// stages, with the block's rates; the forward waves read d-fragments as two 8-byte
+// halves, the contraction waves read the tile transposed (ds_read_b64_tr_b16).
+// Iteration i: forward of block i, contractions of block i-1, DMA of block i+1.
 template <int D>
 struct FastLayout {
   static constexpr int kChunks = D / 8;                   // 16-byte chunks per token row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTile = kTokBlock * kRowBytes;     // one K or V block
-  static constexpr int kStage = 2 * kTile;
-  static constexpr int kStages = 3;
+  static constexpr int kEta = 2 * kTile;                  // the block's 32 rates (fp32), 256 bytes reserved
+  static constexpr int kPk = kEta + 256;                  // packed dZ1, dZ3, H': [wave][3][lane] x 16 bytes
+  static constexpr int kStage = kPk + 4 * 3 * 64 * 16;
 };
 
+typedef unsigned long long u64;
+typedef u64 u64x2 __attribute__((ext_vector_type(2)));
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
+__global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
   using L = FastLayout<D>;
   constexpr int KC = D / 32;   // reduction chunks over d
   constexpr int DT = D / 16;   // 16-wide d tiles of the outputs
-  // three separate arrays (not one indexed array) so that the compiler can tell the
-  // stage being DMA'd from the two being read and need not wait for the DMA
+  // three separate arrays (not one indexed array), each named statically, so that
+  // the compiler can tell the stage being DMA'd from the ones being read
   __shared__ __attribute__((aligned(16))) unsigned char st0[L::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char st1[L::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char st2[L::kStage];
@@ -65,227 +73,253 @@ __global__ __launch_bounds__(256, 1) void grad_fast_kernel(GradParams p) {
   const int split = grp / p.heads;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  // wave index, role and hidden group are wave-uniform: keep them scalar
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool forward_role = wv < 4;
+  const int w = wv & 3;
+  const int l = tid & 63, g = l >> 4, li = l & 15;
   const int hid0 = jt * kHidTile + 16 * w;
 
-  // weights of this wave's 16 hidden units, B-operand fragments over d
-  bf16x8 w1f[KC], w3f[KC], w2f[KC];
-  {
-    const int64_t row = ((int64_t)h * p.m + hid0 + li) * D + 8 * g;
-    const __bf16 *W1 = static_cast<const __bf16 *>(p.w1) + row;
-    const __bf16 *W3 = static_cast<const __bf16 *>(p.w3) + row;
-    const __bf16 *W2 = static_cast<const __bf16 *>(p.w2t) + row;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      w1f[kc] = ld8(W1 + 32 * kc);
-      w3f[kc] = ld8(W3 + 32 * kc);
-      w2f[kc] = ld8(W2 + 32 * kc);
-    }
-  }
-
-  f32x4 a1[DT], a3[DT], a2[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) a1[i] = a3[i] = a2[i] = f32x4{0, 0, 0, 0};
-
-  const int64_t blk0 = (int64_t)split * p.nblk / p.splits;
-  const int64_t blk1 = (int64_t)(split + 1) * p.nblk / p.splits;
+  // token and block indices fit 32 bits (the host limits n): the loop control and
+  // the ragged-block tests stay on the scalar unit
+  const int n = (int)p.n;
+  const int blk0 = (int)((int64_t)split * p.nblk / p.splits);
+  const int blk1 = (int)((int64_t)(split + 1) * p.nblk / p.splits);
+  const int nb = blk1 - blk0;
 
   // Staging: each wave instruction DMAs 1 KB (64 lanes x 16 bytes) of a block
   // straight into LDS.  1 KB piece b of a stage holds matrix b / (NPIECE / 2) and
   // rows kRowsPer * (b % (NPIECE / 2)) ..; lane l fills row r = first + l / kChunks at
   // physical chunk p = l % kChunks, i.e. the logical chunk p ^ swizzle(r) of token
-  // row r.  Rows past n are fetched from row n-1; their rate eta is set to 0, which
-  // zeroes dH, dZ1, dZ3 and H' and so their whole contribution.
+  // row r.  Rows past n are fetched from row n-1; their rate is 0, which zeroes
+  // dH, dZ1, dZ3 and H' and so their whole contribution.
   constexpr int kRowsPer = 1024 / L::kRowBytes;           // token rows per 1 KB piece
-  constexpr int NPIECE = L::kStage / 1024;                // pieces per stage
-  constexpr int PPW = NPIECE / 4;                         // pieces per wave
+  constexpr int NPIECE = 2 * L::kTile / 1024;             // K and V pieces per stage
+  constexpr int PPW = NPIECE / 8;                         // pieces per wave
   const __bf16 *Kh = static_cast<const __bf16 *>(p.k) + (int64_t)h * D;
   const __bf16 *Vh = static_cast<const __bf16 *>(p.v) + (int64_t)h * D;
-  // per-lane byte offset of each piece inside a block (row r, logical chunk) and its row
-  int srow[PPW], soff[PPW];
+  auto piece_row = [&](int q) { return kRowsPer * ((wv * PPW + q) % (NPIECE / 2)) + l / L::kChunks; };
+  unsigned soff[PPW];          // per-lane byte offset of each piece inside a block
+  const unsigned row_bytes = (unsigned)(p.ld * 2);
 #pragma unroll
   for (int q = 0; q < PPW; ++q) {
-    const int piece = w * PPW + q;
-    const int r = kRowsPer * (piece % (NPIECE / 2)) + l / L::kChunks;
-    srow[q] = r;
-    soff[q] = (int)(((int64_t)r * p.ld + 8 * ((l % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)))) * 2);
+    const int r = piece_row(q);
+    soff[q] = (unsigned)r * row_bytes + 16u * (unsigned)((l % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)));
   }
-  auto stage_block = [&](int64_t blk, unsigned char *dst) {
-    const int64_t t0 = blk * kTokBlock;
-    // wave-uniform block bases; per-lane 32-bit offsets (a block spans 32 rows)
-    const char *kb = reinterpret_cast<const char *>(Kh + t0 * p.ld);
-    const char *vb = reinterpret_cast<const char *>(Vh + t0 * p.ld);
-    if (t0 + kTokBlock <= p.n) {                                  // wave-uniform: full block
+  // The rates of a block come with it (wave 0, one dword per lane) through a
+  // range-checked buffer view that ends at token n: rates past n arrive as 0.
+  const float *eta = p.eta + (int64_t)h * p.eta_hs;
+  auto stage_block = [&](int blk, unsigned char *dst) {
+    const int t0 = blk * kTokBlock;
+    if (wv == 0) {
+      const int valid = n - t0 < kTokBlock ? n - t0 : kTokBlock;
+      const __amdgpu_buffer_rsrc_t er =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(eta + t0), (short)0, valid * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void *)(dst + L::kEta), 4,
+                                               4u * (unsigned)l, 0, 0, 0);
+    }
+    // wave-uniform block bases; unsigned per-lane 32-bit offsets (a block spans 32 rows)
+    const char *kb = reinterpret_cast<const char *>(Kh + (int64_t)t0 * p.ld);
+    const char *vb = reinterpret_cast<const char *>(Vh + (int64_t)t0 * p.ld);
+    if (t0 + kTokBlock <= n) {                                    // wave-uniform: full block
 #pragma unroll
       for (int q = 0; q < PPW; ++q) {
-        const int piece = w * PPW + q;
+        const int piece = wv * PPW + q;
         copy16_to_lds((piece >= NPIECE / 2 ? vb : kb) + soff[q], dst + piece * 1024);
       }
     } else {                                                      // last block: clamp rows to n-1
 #pragma unroll
       for (int q = 0; q < PPW; ++q) {
-        const int piece = w * PPW + q;
-        const int r = srow[q];
-        const int64_t shift = (t0 + r < p.n) ? 0 : (p.n - 1 - t0 - r) * p.ld * 2;
-        copy16_to_lds((piece >= NPIECE / 2 ? vb : kb) + soff[q] + shift, dst + piece * 1024);
+        const int piece = wv * PPW + q;
+        const int r = piece_row(q), keep = n - 1 - t0;
+        const unsigned off = r <= keep ? soff[q] : soff[q] - (unsigned)(r - keep) * row_bytes;
+        copy16_to_lds((piece >= NPIECE / 2 ? vb : kb) + off, dst + piece * 1024);
       }
     }
   };
-
-  // eta of this lane's 8 tokens 8g .. 8g+7 of a block (0 past n), loaded one block ahead
-  const float *eta = p.eta + (int64_t)h * p.eta_hs;
-  float en[8];
-  auto load_eta = [&](int64_t blk) {
-    const int64_t t0 = blk * kTokBlock + 8 * g;
-    if (blk * kTokBlock + kTokBlock <= p.n) {                   // wave-uniform: block is full
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(eta + t0);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(eta + t0 + 4);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) en[v] = a[v], en[4 + v] = b[v];
-    } else {
-#pragma unroll
-      for (int v = 0; v < 8; ++v) en[v] = (t0 + v < p.n) ? eta[t0 + v] : 0.0f;
-    }
-  };
-
-  // LDS addresses.  Chunk indices 4kc + g (d-reductions) and 2dt + e (token
-  // reductions) share no bits with the loop counter's XOR partner, so with the
-  // swizzle s of a row:  ((4kc + g) ^ s) * 16 = (16 (g ^ s)) ^ 64 kc  and
-  // ((2dt + e) ^ s) * 16 = (16 (e ^ s)) ^ 32 dt: one XOR per read.
-  // d-reductions: row perm_row(u, li), chunk 4kc + g.
-  int base_a[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int rt = perm_row(u, li);
-    base_a[u] = rt * L::kRowBytes + 16 * (g ^ (swz_rows(rt) & (L::kChunks - 1)));
-  }
-  // token reductions (transposed reads): lane (g, li) supplies row 8g + 4q + li/4,
-  // column 16 dt + 4 (li % 4) and receives rows 8g + 4q .. +3 of column 16 dt + li.
-  int base_b[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 8 * g + 4 * q + (li >> 2);
-    const int e = (li & 3) >> 1;
-    base_b[q] = row * L::kRowBytes + 16 * (e ^ (swz_rows(row) & (L::kChunks - 1))) + 8 * (li & 1);
-  }
-
-  // d-reductions of one block: z1 = K W1^T, z3 = K W3^T, p = V W2 for this wave's
-  // 16 hidden units; rows = tokens perm_row(u, li); fragments one chunk ahead
-  f32x4 z1[2], z3[2], pp[2];
-  auto forward = [&](const unsigned char *base) {
-    constexpr int NA = 2 * KC;
-    bf16x8 kf[2], vf[2];
-    auto lda = [&](int i, int slot) {
-      const int u = i / KC, kc = i % KC;
-      const unsigned char *pk = base + (base_a[u] ^ (64 * kc));
-      kf[slot] = *reinterpret_cast<const bf16x8 *>(pk);
-      vf[slot] = *reinterpret_cast<const bf16x8 *>(pk + L::kTile);
-    };
-    lda(0, 0);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int u = i / KC, kc = i % KC;
-      if (kc == 0) z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
-      if (i + 1 < NA) lda(i + 1, (i + 1) & 1);
-      z1[u] = mma(kf[i & 1], w1f[kc], z1[u]);
-      z3[u] = mma(kf[i & 1], w3f[kc], z3[u]);
-      pp[u] = mma(vf[i & 1], w2f[kc], pp[u]);
-    }
-  };
-  // SwiGLU backward of element v = 4u + r (token 8g + v, hidden hid0 + li)
-  float dz1v[8], dz3v[8], hv[8];
-  auto backward_elem = [&](int v, const float *e) {
-    const int u = v >> 2, r = v & 3;
-    const float z = z1[u][r], y = z3[u][r], ne = e[v];
-    const float sg = sigmoid_fast(z);
-    const float act = z * sg;
-    const float dh = ne * pp[u][r];
-    dz3v[v] = dh * act;
-    dz1v[v] = dh * y * (sg + act - act * sg);
-    hv[v] = ne * (act * y);
-  };
-  // token contractions of a block: G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H', with
-  // the SwiGLU backward of the next block (if any) interleaved between the MFMAs
-  bf16x8 dz1f, dz3f, hf;
-  auto contract = [&](const unsigned char *base, bool with_backward, const float *e) {
-    bf16x8 ktf[2], vtf[2];
-    auto ldb = [&](int dt, int slot) {
-      const unsigned char *p0 = base + (base_b[0] ^ (32 * dt));
-      const unsigned char *p1 = base + (base_b[1] ^ (32 * dt));
-      ktf[slot] = cat8(lds_read_tr16(p0), lds_read_tr16(p1));
-      vtf[slot] = cat8(lds_read_tr16(p0 + L::kTile), lds_read_tr16(p1 + L::kTile));
-    };
-    ldb(0, 0);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      if (dt + 1 < DT) ldb(dt + 1, (dt + 1) & 1);
-      a1[dt] = mma(dz1f, ktf[dt & 1], a1[dt]);
-      a3[dt] = mma(dz3f, ktf[dt & 1], a3[dt]);
-      a2[dt] = mma(vtf[dt & 1], hf, a2[dt]);
-      if (with_backward)   // the 8 backward elements spread evenly over the DT steps
-#pragma unroll
-        for (int v = dt * 8 / DT; v < (dt + 1) * 8 / DT; ++v) backward_elem(v, e);
-    }
-  };
-  auto pack = [&]() {
-    dz1f = pack8<__bf16>(dz1v);
-    dz3f = pack8<__bf16>(dz3v);
-    hf = pack8<__bf16>(hv);
-  };
-
-  if (blk0 < blk1) {
-    load_eta(blk0);
-    stage_block(blk0, st0);
-    if (blk0 + 1 < blk1) stage_block(blk0 + 1, st1);
+  auto sync = [&]() {
     wait_all_memory();
     __syncthreads();
-    // prologue: forward and backward of the first block
-    float e[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) e[v] = -en[v];
-    if (blk0 + 1 < blk1) load_eta(blk0 + 1);
-    forward(st0);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) backward_elem(v, e);
-    pack();
-    // block blk lives in stage (blk - blk0) % 3
-    auto iteration = [&](int64_t blk, const unsigned char *cur, const unsigned char *prev, unsigned char *next) {
-      // consume the prefetched rates before issuing new memory operations, so that
-      // no wait for them can also wait for the DMA issued below
-#pragma unroll
-      for (int v = 0; v < 8; ++v) e[v] = -en[v];
-      if (blk + 1 < blk1) {
-        load_eta(blk + 1);
-        stage_block(blk + 1, next);     // into the stage freed by block blk-2
-      }
-      forward(cur);
-      contract(prev, true, e);          // block blk-1's contractions + block blk's backward
-      pack();
-      wait_all_memory();
-      __syncthreads();
-    };
-    for (int64_t blk = blk0 + 1; blk < blk1; blk += 3) {
-      iteration(blk, st1, st0, st2);
-      if (blk + 1 < blk1) iteration(blk + 1, st2, st1, st0);
-      if (blk + 2 < blk1) iteration(blk + 2, st0, st2, st1);
-    }
-    const int last = (int)((blk1 - 1 - blk0) % 3);
-    contract(last == 0 ? st0 : (last == 1 ? st1 : st2), false, e);
-  }
+  };
+  // this lane's 16-byte slot of operand op in the packed-operand area of a stage
+  const int pk_slot = L::kPk + ((w * 3) * 64 + l) * 16;
 
-  // partials: G1/G3 rows hid0 + 4g + r, cols 16 dt + li;  G2 rows 16 dt + 4g + r, cols hid0 + li
-  const int64_t mat = (int64_t)p.m * D;
-  float *P1 = p.part + ((int64_t)split * 3 * p.heads + h) * mat;
-  float *P3 = P1 + p.heads * mat;
-  float *P2 = P3 + p.heads * mat;
+  if (nb > 0) {
+    stage_block(blk0, st0);
+    sync();
+  }
+  // Both roles run iterations i = 0 .. nb with one barrier each: the forward waves
+  // idle in the last, the contraction waves in the first.  Block blk0 + i lives in
+  // stage i % 3; the loop is unrolled by 3 so that every stage is named statically.
+  if (forward_role) {
+    // d-reduction fragments are read as two 8-byte halves; odd lane groups take the
+    // upper half first, which spreads one read over all 64 banks.  The MFMA only
+    // needs A and B to agree on the k order, so the weights use the same order.
+    const int hs = (g & 1) * 8;
+    bf16x8 w1f[KC], w3f[KC], w2f[KC];   // B-operand fragments over d, this wave's 16 hidden units
+    {
+      const int64_t row = ((int64_t)h * p.m + hid0 + li) * D + 8 * g;
+      const char *W1 = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.w1) + row);
+      const char *W3 = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.w3) + row);
+      const char *W2 = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.w2t) + row);
+      auto frag = [&](const char *src) {
+        const u64 lo = *reinterpret_cast<const u64 *>(src + hs), hi = *reinterpret_cast<const u64 *>(src + 8 - hs);
+        return __builtin_bit_cast(bf16x8, u64x2{lo, hi});
+      };
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      P1[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a1[dt][r];
-      P3[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a3[dt][r];
-      P2[(int64_t)(16 * dt + 4 * g + r) * p.m + hid0 + li] = a2[dt][r];
+      for (int kc = 0; kc < KC; ++kc) {
+        w1f[kc] = frag(W1 + 64 * kc);
+        w3f[kc] = frag(W3 + 64 * kc);
+        w2f[kc] = frag(W2 + 64 * kc);
+      }
     }
+    // LDS addresses.  Chunk 4kc + g of row rt with swizzle s: ((4kc + g) ^ s) * 16 =
+    // (16 (g ^ s)) ^ 64 kc, one XOR per read; rows perm_row(u, li).
+    int base_a[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rt = perm_row(u, li);
+      const int a = rt * L::kRowBytes + 16 * (g ^ (swz_rows(rt) & (L::kChunks - 1)));
+      base_a[u][0] = a + hs;
+      base_a[u][1] = a + 8 - hs;
+    }
+    // forward + backward of the block in stage `cur`; packed operands into `cur`
+    auto forward_block = [&](unsigned char *cur) {
+      f32x4 z1[2], z3[2], pp[2];
+      bf16x8 kf[2], vf[2];
+      auto lda = [&](int i, int slot) {
+        const int u = i / KC, kc = i % KC;
+        // V's addresses pass through an empty asm: otherwise the K and V halves
+        // (16 KB apart) merge into paired reads whose results need register moves
+        int v0 = base_a[u][0] ^ (64 * kc), v1 = base_a[u][1] ^ (64 * kc);
+        const unsigned char *p0 = cur + v0, *p1 = cur + v1;
+        asm volatile("" : "+v"(v0), "+v"(v1));
+        const unsigned char *q0 = cur + L::kTile + v0, *q1 = cur + L::kTile + v1;
+        kf[slot] = __builtin_bit_cast(bf16x8, u64x2{*reinterpret_cast<const u64 *>(p0),
+                                                    *reinterpret_cast<const u64 *>(p1)});
+        vf[slot] = __builtin_bit_cast(bf16x8, u64x2{*reinterpret_cast<const u64 *>(q0),
+                                                    *reinterpret_cast<const u64 *>(q1)});
+      };
+      constexpr int NA = 2 * KC;
+      lda(0, 0);
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int u = i / KC, kc = i % KC;
+        if (kc == 0) z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
+        if (i + 1 < NA) lda(i + 1, (i + 1) & 1);
+        z1[u] = mma(kf[i & 1], w1f[kc], z1[u]);
+        z3[u] = mma(kf[i & 1], w3f[kc], z3[u]);
+        pp[u] = mma(vf[i & 1], w2f[kc], pp[u]);
+      }
+      // rates of this lane's tokens 8g .. 8g+7
+      const f32x4 ea = *reinterpret_cast<const f32x4 *>(cur + L::kEta + 32 * g);
+      const f32x4 eb = *reinterpret_cast<const f32x4 *>(cur + L::kEta + 32 * g + 16);
+      // SwiGLU backward of element v = 4u + r (token 8g + v, hidden hid0 + li), with
+      // dL/df = -eta v:  dH = -eta p
+      bf16x8 pk1, pk3, pkh;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int u = v >> 2, r = v & 3;
+        const float ne = -(v < 4 ? ea[v] : eb[v - 4]);
+        const float z = z1[u][r], y = z3[u][r];
+        const float sg = sigmoid_fast(z);
+        const float act = z * sg;
+        const float dh = ne * pp[u][r];
+        pk3[v] = (__bf16)(dh * act);
+        pk1[v] = (__bf16)(dh * y * (sg + act - act * sg));
+        pkh[v] = (__bf16)(ne * (act * y));
+      }
+      *reinterpret_cast<bf16x8 *>(cur + pk_slot) = pk1;
+      *reinterpret_cast<bf16x8 *>(cur + pk_slot + 1024) = pk3;
+      *reinterpret_cast<bf16x8 *>(cur + pk_slot + 2048) = pkh;
+    };
+    auto step = [&](int i, unsigned char *cur, unsigned char *next) {
+      if (i + 1 < nb) stage_block(blk0 + i + 1, next);
+      forward_block(cur);
+      sync();
+    };
+    int i = 0;
+    for (; i + 3 <= nb; i += 3) {
+      step(i, st0, st1);
+      step(i + 1, st1, st2);
+      step(i + 2, st2, st0);
+    }
+    if (i < nb) step(i, st0, st1);
+    if (i + 1 < nb) step(i + 1, st1, st2);
+    if (nb > 0) sync();                // iteration nb: the contraction of the last block
+  } else {
+    f32x4 a1[DT], a3[DT], a2[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) a1[t] = a3[t] = a2[t] = f32x4{0, 0, 0, 0};
+    // transposed reads: lane (g, li) supplies row 8g + 4q + li/4, column 16 dt + 4 (li % 4)
+    // and receives rows 8g + 4q .. +3 of column 16 dt + li; chunk 2dt + e of row r with
+    // swizzle s: ((2dt + e) ^ s) * 16 = (16 (e ^ s)) ^ 32 dt
+    int base_b[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = 8 * g + 4 * q + (li >> 2);
+      const int e = (li & 3) >> 1;
+      base_b[q] = row * L::kRowBytes + 16 * (e ^ (swz_rows(row) & (L::kChunks - 1))) + 8 * (li & 1);
+    }
+    // G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H' for the block in stage `prev`
+    auto contract_block = [&](const unsigned char *prev) {
+      const bf16x8 pk1 = *reinterpret_cast<const bf16x8 *>(prev + pk_slot);
+      const bf16x8 pk3 = *reinterpret_cast<const bf16x8 *>(prev + pk_slot + 1024);
+      const bf16x8 pkh = *reinterpret_cast<const bf16x8 *>(prev + pk_slot + 2048);
+      bf16x8 ktf[2], vtf[2];
+      auto ldb = [&](int dt, int slot) {
+        // the bases pass through an empty asm so that each address is formed (one
+        // XOR) right before its read instead of 32 of them being held in registers
+        int b0 = base_b[0], b1 = base_b[1];
+        asm volatile("" : "+v"(b0), "+v"(b1));
+        const unsigned char *p0 = prev + (b0 ^ (32 * dt));
+        const unsigned char *p1 = prev + (b1 ^ (32 * dt));
+        ktf[slot] = cat8(lds_read_tr16(p0), lds_read_tr16(p1));
+        vtf[slot] = cat8(lds_read_tr16(p0 + L::kTile), lds_read_tr16(p1 + L::kTile));
+      };
+      ldb(0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        if (dt + 1 < DT) ldb(dt + 1, (dt + 1) & 1);
+        a1[dt] = mma(pk1, ktf[dt & 1], a1[dt]);
+        a3[dt] = mma(pk3, ktf[dt & 1], a3[dt]);
+        a2[dt] = mma(vtf[dt & 1], pkh, a2[dt]);
+      }
+    };
+    auto step = [&](int i, const unsigned char *prev, unsigned char *next) {
+      if (i + 1 < nb) stage_block(blk0 + i + 1, next);
+      if (i > 0) contract_block(prev);
+      sync();
+    };
+    // iteration i: contraction of block i - 1 (stage (i - 1) % 3), DMA of block i + 1
+    int i = 0;
+    for (; i + 3 <= nb; i += 3) {
+      step(i, st2, st1);
+      step(i + 1, st0, st2);
+      step(i + 2, st1, st0);
+    }
+    if (i < nb) step(i, st2, st1);
+    if (i + 1 < nb) step(i + 1, st0, st2);
+    if (nb > 0) {                      // iteration nb: the last block, stage (nb - 1) % 3
+      const int last = (nb - 1) % 3;
+      contract_block(last == 0 ? st0 : (last == 1 ? st1 : st2));
+      sync();
+    }
+
+    // partials: G1/G3 rows hid0 + 4g + r, cols 16 dt + li;  G2 rows 16 dt + 4g + r, cols hid0 + li
+    const int64_t mat = (int64_t)p.m * D;
+    float *P1 = p.part + ((int64_t)split * 3 * p.heads + h) * mat;
+    float *P3 = P1 + p.heads * mat;
+    float *P2 = P3 + p.heads * mat;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        P1[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a1[dt][r];
+        P3[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a3[dt][r];
+        P2[(int64_t)(16 * dt + 4 * g + r) * p.m + hid0 + li] = a2[dt][r];
+      }
+  }
 }
 
 // ------------------------------------------------------------- general path
@@ -433,9 +467,10 @@ int grad_general_dc(int d, bool bf16) {
 hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int grid, hipStream_t s) {
   if (fast) {
     switch (d) {
-      case 64: hipLaunchKernelGGL(grad_fast_kernel<64>, dim3(grid), dim3(256), 0, s, p); break;
-      case 128: hipLaunchKernelGGL(grad_fast_kernel<128>, dim3(grid), dim3(256), 0, s, p); break;
-      case 256: hipLaunchKernelGGL(grad_fast_kernel<256>, dim3(grid), dim3(256), 0, s, p); break;
+      // 8 waves: 4 forward + 4 contraction (see grad_fast_kernel)
+      case 64: hipLaunchKernelGGL(grad_fast_kernel<64>, dim3(grid), dim3(512), 0, s, p); break;
+      case 128: hipLaunchKernelGGL(grad_fast_kernel<128>, dim3(grid), dim3(512), 0, s, p); break;
+      case 256: hipLaunchKernelGGL(grad_fast_kernel<256>, dim3(grid), dim3(512), 0, s, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -194,11 +194,11 @@ hipError_t cast_impl(const float *w1, const float *w3, const float *w2, void *w1
 //   A = X X^T           (P = Q = X,  K = c)
 //   A A                 (P = Q = A,  K = r; A is symmetric)
 //   B X                 (P = B, Q = X^T, K = r; X^T is kept alongside X)
-// on 64x64 output tiles, 4 waves of 32x32, K staged through LDS 32 at a time
+// on 64x64 output tiles, 4 waves of 32x32, K staged through LDS 64 at a time
 // with the next chunk's loads in flight.
 
 constexpr int kT = 64;        // output tile
-constexpr int kKc = 32;       // K chunk
+constexpr int kKc = 64;       // K chunk
 constexpr int kLdsW = kKc + 4;
 
 struct NsSmem {
@@ -216,39 +216,42 @@ struct NsSmem {
 __device__ __forceinline__ void tile_nt(const float *__restrict__ P, int ldp, const float *__restrict__ Q, int ldq,
                                         int K, NsSmem &sm, f32x4 acc[2][2]) {
   const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
-  const int lr = t >> 3, lc = (t & 7) * 4;          // loader: rows lr, lr + 32; 4 floats at lc
+  const int lr = t >> 4, lc = (t & 15) * 4;         // loader: rows lr + 16 u; 4 floats at lc
 #pragma unroll
   for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x4{0, 0, 0, 0};
-  f32x4 pa[2], pb[2];
+  f32x4 pa[4], pb[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 32 * u) * ldp + lc);
-    pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 32 * u) * ldq + lc);
+  for (int u = 0; u < 4; ++u) {
+    pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 16 * u) * ldp + lc);
+    pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 16 * u) * ldq + lc);
   }
   const int nk = K / kKc;
   for (int kc = 0; kc < nk; ++kc) {
     const int buf = kc & 1;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      *reinterpret_cast<f32x4 *>(&sm.g.a[buf][lr + 32 * u][lc]) = pa[u];
-      *reinterpret_cast<f32x4 *>(&sm.g.b[buf][lr + 32 * u][lc]) = pb[u];
+    for (int u = 0; u < 4; ++u) {
+      *reinterpret_cast<f32x4 *>(&sm.g.a[buf][lr + 16 * u][lc]) = pa[u];
+      *reinterpret_cast<f32x4 *>(&sm.g.b[buf][lr + 16 * u][lc]) = pb[u];
     }
     __syncthreads();
     if (kc + 1 < nk) {
       const int k0 = (kc + 1) * kKc;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 32 * u) * ldp + k0 + lc);
-        pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 32 * u) * ldq + k0 + lc);
+      for (int u = 0; u < 4; ++u) {
+        pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 16 * u) * ldp + k0 + lc);
+        pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 16 * u) * ldq + k0 + lc);
       }
     }
     const int ra = (w >> 1) * 32 + li, rb = (w & 1) * 32 + li;
-    const f32x8 a0 = ld8(&sm.g.a[buf][ra][8 * g]), a1 = ld8(&sm.g.a[buf][ra + 16][8 * g]);
-    const f32x8 b0 = ld8(&sm.g.b[buf][rb][8 * g]), b1 = ld8(&sm.g.b[buf][rb + 16][8 * g]);
-    acc[0][0] = mma(a0, b0, acc[0][0]);
-    acc[0][1] = mma(a0, b1, acc[0][1]);
-    acc[1][0] = mma(a1, b0, acc[1][0]);
-    acc[1][1] = mma(a1, b1, acc[1][1]);
+#pragma unroll
+    for (int kk = 0; kk < kKc; kk += 32) {
+      const f32x8 a0 = ld8(&sm.g.a[buf][ra][kk + 8 * g]), a1 = ld8(&sm.g.a[buf][ra + 16][kk + 8 * g]);
+      const f32x8 b0 = ld8(&sm.g.b[buf][rb][kk + 8 * g]), b1 = ld8(&sm.g.b[buf][rb + 16][kk + 8 * g]);
+      acc[0][0] = mma(a0, b0, acc[0][0]);
+      acc[0][1] = mma(a0, b1, acc[0][1]);
+      acc[1][0] = mma(a1, b0, acc[1][0]);
+      acc[1][1] = mma(a1, b1, acc[1][1]);
+    }
   }
 }
 
