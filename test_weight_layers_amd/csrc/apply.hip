@@ -13,13 +13,19 @@ namespace ttt {
 namespace {
 
 constexpr int kHidChunk = 32;
+#ifndef APPLY_WAVES
+#define APPLY_WAVES 8
+#endif
+constexpr int kApplyWaves = APPLY_WAVES;   // waves (of 32 tokens) per fast workgroup
 
 // ---------------------------------------------------------------- fast path
-// bf16, D <= 256.  A workgroup owns 128 tokens of one head (32 per wave); each
-// wave keeps its Q fragments and its O^T accumulators in registers.  The head's
-// weights stream through LDS 32 hidden units at a time: W1 and W3 rows and W2^T
-// rows ([hidden][d], so the second product reads them with the transposing load),
-// DMA'd into one of two separate stage arrays while the other is consumed.
+// bf16, D <= 256.  A workgroup owns 32 WV tokens of one head (32 per wave, WV
+// waves, two per SIMD when WV = 8); each wave keeps its Q fragments and its O^T
+// accumulators in registers.  The head's weights stream through LDS 32 hidden
+// units at a time: W1 and W3 rows and W2^T rows ([hidden][d], so the second
+// product reads them with the transposing load), DMA'd into one of two separate
+// stage arrays while the other is consumed.  Every weight byte fetched serves
+// 32 WV tokens, so the tile is as tall as the register file allows.
 template <int D>
 struct ApplyLayout {
   static constexpr int kChunks = D / 8;
@@ -28,11 +34,11 @@ struct ApplyLayout {
   static constexpr int kStage = 3 * kTile;              // W1, W3, W2^T
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
+template <int D, int WV>
+__global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
   using L = ApplyLayout<D>;
   constexpr int KC = D / 32, DT = D / 16;
-  constexpr int NPIECE = L::kStage / 1024, PPW = NPIECE / 4, kRowsPer = 1024 / L::kRowBytes;
+  constexpr int NPIECE = L::kStage / 1024, PPW = (NPIECE + WV - 1) / WV, kRowsPer = 1024 / L::kRowBytes;
   constexpr int PPT = NPIECE / 3;                        // 1 KB pieces per tile
   __shared__ __attribute__((aligned(16))) unsigned char sa[L::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char sb[L::kStage];
@@ -40,8 +46,8 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
   const int h = blockIdx.x % p.heads;
   const int64_t tile = blockIdx.x / p.heads;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
-  const int64_t tok0 = tile * 128 + 32 * w;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, li = l & 15;
+  const int64_t tok0 = tile * (32 * WV) + 32 * w;
 
   // Q^T fragments (B operand): token tok0 + 16t + li, d = 32 kc + 8g .. +8
   bf16x8 qf[2][KC];
@@ -63,21 +69,24 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
   // fills row r at physical chunk l % kChunks = logical chunk ^ swizzle(tile, r).
   const char *wsrc[3] = {static_cast<const char *>(p.w1), static_cast<const char *>(p.w3),
                          static_cast<const char *>(p.w2t)};
-  int soff[PPW];
-#pragma unroll
-  for (int q = 0; q < PPW; ++q) {
-    const int piece = w * PPW + q, mat = piece / PPT;
-    const int r = kRowsPer * (piece % PPT) + l / L::kChunks;
+  // offset of piece q in a chunk, formed at each use (the lane index passes through
+  // an empty asm) rather than held in registers
+  auto piece_off = [&](int q) {
+    int lw = l;
+    asm volatile("" : "+v"(lw));
+    const int piece = w * PPW + q, mat = piece < NPIECE ? piece / PPT : 0;
+    const int r = kRowsPer * (piece % PPT) + lw / L::kChunks;
     const int sw = (mat < 2 ? swz_rows_b128(r) : swz_rows(r)) & (L::kChunks - 1);
-    soff[q] = (r * D + 8 * ((l % L::kChunks) ^ sw)) * 2;
-  }
+    return (r * D + 8 * ((lw % L::kChunks) ^ sw)) * 2;
+  };
   const int64_t head_off = (int64_t)h * p.m * D * 2;
   auto stage_chunk = [&](int hc, unsigned char *dst) {
     const int64_t base = head_off + (int64_t)hc * kHidChunk * D * 2;   // wave-uniform
 #pragma unroll
     for (int q = 0; q < PPW; ++q) {
       const int piece = w * PPW + q;
-      copy16_to_lds(wsrc[piece / PPT] + base + soff[q], dst + piece * 1024);
+      if (NPIECE % WV != 0 && piece >= NPIECE) break;     // wave-uniform
+      copy16_to_lds(wsrc[piece / PPT] + base + piece_off(q), dst + piece * 1024);
     }
   };
 
@@ -107,7 +116,9 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
       for (int t = 0; t < 2; ++t) z1[u][t] = z3[u][t] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const unsigned char *pa = base + (base_a[u] ^ (64 * kc));
+        int ba = base_a[u];                 // one XOR per read rather than held addresses
+        asm volatile("" : "+v"(ba));
+        const unsigned char *pa = base + (ba ^ (64 * kc));
         const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(pa);
         const bf16x8 a3 = *reinterpret_cast<const bf16x8 *>(pa + L::kTile);
 #pragma unroll
@@ -134,8 +145,9 @@ __global__ __launch_bounds__(256, 1) void apply_fast_kernel(ApplyParams p) {
     // O^T[d][tok] += W2[d][chunk] H^T
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 w2f = cat8(lds_read_tr16(base + (base_b[0] ^ (32 * dt))),
-                              lds_read_tr16(base + (base_b[1] ^ (32 * dt))));
+      int b0 = base_b[0], b1 = base_b[1];
+      asm volatile("" : "+v"(b0), "+v"(b1));
+      const bf16x8 w2f = cat8(lds_read_tr16(base + (b0 ^ (32 * dt))), lds_read_tr16(base + (b1 ^ (32 * dt))));
       acc[dt][0] = mma(w2f, hf[0], acc[dt][0]);
       acc[dt][1] = mma(w2f, hf[1], acc[dt][1]);
     }
@@ -267,12 +279,12 @@ int apply_general_dc(int d, bool) { return d < 128 ? d : 128; }
 
 hipError_t launch_apply(const ApplyParams &p, int d, bool bf16, bool fast, hipStream_t s) {
   if (fast) {
-    const int64_t grid = (p.nq + 127) / 128 * p.heads;
+    const int64_t grid = (p.nq + 32 * kApplyWaves - 1) / (32 * kApplyWaves) * p.heads;
     if (grid == 0) return hipSuccess;
     switch (d) {
-      case 64: hipLaunchKernelGGL(apply_fast_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
-      case 128: hipLaunchKernelGGL(apply_fast_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
-      case 256: hipLaunchKernelGGL(apply_fast_kernel<256>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((apply_fast_kernel<64, kApplyWaves>), dim3((unsigned)grid), dim3(64 * kApplyWaves), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((apply_fast_kernel<128, kApplyWaves>), dim3((unsigned)grid), dim3(64 * kApplyWaves), 0, s, p); break;
+      case 256: hipLaunchKernelGGL((apply_fast_kernel<256, kApplyWaves>), dim3((unsigned)grid), dim3(64 * kApplyWaves), 0, s, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
