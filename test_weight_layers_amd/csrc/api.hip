@@ -120,7 +120,7 @@ struct UpdatePlan {
   bool bf16, fast, xcd;
   int dchunks, splits, grid;
   int64_t n, nblk;
-  size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_xt0, off_xt1, off_a, off_b, total;
+  size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_xt0, off_xt1, off_a, off_b, off_sync, total;
 };
 
 UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
@@ -164,6 +164,8 @@ UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
   off = align256(off + (size_t)3 * H * p.r * p.r * 4);
   p.off_b = off;
   off = align256(off + (size_t)3 * H * p.r * p.r * 4);
+  p.off_sync = off;
+  off = align256(off + (size_t)H * p.splits * 4);
   p.total = off;
   return p;
 }
@@ -192,7 +194,7 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
               bool ops_ready = false, bool keep_ops = false) {
   const bool fused = !g_ns_unfused;
   const size_t mat = (size_t)P.H * P.d * P.m;
-  void *wop = ws + P.off_wop;
+  void *const wop = ws + P.off_wop;
   float *part = reinterpret_cast<float *>(ws + P.off_part);
   float *g = reinterpret_cast<float *>(ws + P.off_g);
   float *sumsq = reinterpret_cast<float *>(ws + P.off_sumsq);
@@ -229,7 +231,15 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
     }
     gp.part = part, gp.n = P.n, gp.nblk = P.nblk;
     gp.heads = P.H, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
-    st = run(TTT_K_GRAD, "gradient", s, [&] { return launch_grad(gp, P.d, P.bf16, P.fast, P.grid, s); });
+    // the hidden tiles of a token range keep pace through these counters (see the kernel)
+    if (P.fast && P.xcd) gp.group_sync = reinterpret_cast<unsigned *>(ws + P.off_sync);
+    st = run(TTT_K_GRAD, "gradient", s, [&] {
+      if (gp.group_sync) {
+        const hipError_t e = launch_zero_u32(gp.group_sync, P.H * P.splits, s);
+        if (e != hipSuccess) return e;
+      }
+      return launch_grad(gp, P.d, P.bf16, P.fast, P.grid, s);
+    });
     if (st) return st;
     if (fused) {
       NsStepParams np{};

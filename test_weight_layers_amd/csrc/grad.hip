@@ -141,6 +141,27 @@ __global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
     wait_all_memory();
     __syncthreads();
   };
+  // Pace keeping.  The m / 64 workgroups of one token range (one per hidden tile)
+  // run on one XCD and read the same K/V blocks, which its L2 serves once while they
+  // stay close; left alone they drift apart over thousands of blocks until the L2
+  // no longer holds a block between its readers.  Every kPace blocks, wave 0 counts
+  // the workgroup in at its group's counter and waits (bounded: the wait is only a
+  // hint, nothing depends on it) until every workgroup of the group has passed the
+  // previous checkpoint, so they stay within 2 kPace blocks of each other.
+  constexpr int kPace = 32;
+  unsigned *const pace = p.group_sync ? p.group_sync + split * p.heads + h : nullptr;
+  auto keep_pace = [&](int i) {
+    if (pace == nullptr || (i + 1) % kPace != 0 || wv != 0) return;
+    if (l == 0) {
+      const unsigned c = (unsigned)((i + 1) / kPace);
+      __hip_atomic_fetch_add(pace, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned target = (unsigned)mtiles * (c - 1);
+      for (int spin = 0; spin < 256; ++spin) {
+        if (__hip_atomic_load(pace, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+  };
   // this lane's 16-byte slot of operand op in the packed-operand area of a stage
   const int pk_slot = L::kPk + ((w * 3) * 64 + l) * 16;
 
@@ -236,6 +257,7 @@ __global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
     auto step = [&](int i, unsigned char *cur, unsigned char *next) {
       if (i + 1 < nb) stage_block(blk0 + i + 1, next);
       forward_block(cur);
+      keep_pace(i);
       sync();
     };
     int i = 0;
@@ -455,7 +477,18 @@ hipError_t launch_general_d(const GradParams &p, int d, int grid, hipStream_t s)
   return hipErrorInvalidValue;
 }
 
+__global__ __launch_bounds__(256) void zero_u32_kernel(unsigned *p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_u32(unsigned *p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 bool grad_fast_supported(int d, bool bf16) { return bf16 && (d == 64 || d == 128 || d == 256); }
 

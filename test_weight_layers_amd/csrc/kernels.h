@@ -21,6 +21,7 @@ struct GradParams {
   float *part;               // [splits][3][H][m*d] fp32 partial gradients
   int64_t n, nblk;           // tokens, ceil(n / kTokBlock)
   int heads, m, splits, dchunks, xcd_map;
+  unsigned *group_sync;      // fast kernel: [H * splits] progress counters, zero at launch (or null)
 };
 
 struct ApplyParams {
@@ -40,6 +41,8 @@ struct ApplyParams {
 bool grad_fast_supported(int d, bool bf16);
 int grad_general_dc(int d, bool bf16);      // output d-chunk width of the general kernel
 hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int grid, hipStream_t s);
+// Zeroes n 32-bit words (a kernel, not a memset, so that it can sit in a captured graph).
+hipError_t launch_zero_u32(unsigned *p, int n, hipStream_t s);
 
 bool apply_fast_supported(int d, bool bf16);
 int apply_general_dc(int d, bool bf16);
