@@ -79,6 +79,13 @@ def test_tttlrm_width_768_general():
     _check(CONFIGS["c2"], n=1500, nq_extra=300)
 
 
+def test_zipmap_single_head_1024_2048():
+    # the ZipMap layer's own shape (one head, d = 1024, m = 2048, state 6 d^2): the
+    # general kernels, the 1024 x 2048 Newton-Schulz products, a ragged token tail
+    from test_weight_layers_amd.configs import CONFIGS
+    _check(CONFIGS["zipmap1h"], n=1500, nq_extra=77)
+
+
 def test_two_inner_steps_with_conv():
     cfg = cfg_like("c3", frames=2)
     _check(cfg, steps=2)
