@@ -6,5 +6,6 @@ product path never calls it.
 """
 from .lact import (  # noqa: F401
     NS_A, NS_B, NS_C, NS_EPS, NS_ITERS, apply, apply_head, dot_product_loss, gradient,
-    layer, newton_schulz, shortconv2d, silu, sigmoid, stream, swiglu, update, update_head,
+    layer, newton_schulz, norm_preserving_step, output_gate, rms_norm, shortconv2d, silu, sigmoid, stream,
+    swiglu, update, update_head,
 )

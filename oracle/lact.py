@@ -49,6 +49,15 @@ from the pages):
   bias, over each frame's grid_h x grid_w patch tokens (row-major, after the
   frame's n_special leading tokens, which pass through unchanged).
 * Streaming: per chunk, apply with the current W, then update W from the chunk.
+* Norm-preserving step ([ZipMap] 关键设计 3, optional): the page writes
+  W^ = ||W|| (W - Delta) / ||W - Delta|| with Delta = NewtonSchulz(g); here
+  Delta = lr * NS(G) (lr = 1 is the page's form), ||.|| is the Frobenius norm of
+  each weight matrix of each head, ||W|| is taken before the step, and when
+  W - Delta is the zero matrix the result is that zero matrix.
+* Gated output ([ZipMap] 关键设计 3, optional): o = RMSNorm(o') * SiLU(W_g o')
+  acts on the whole output row o' (all H*d channels), W_g is a [C][C] matrix
+  (row = output channel, no bias), RMSNorm(x) = gamma * x / sqrt(mean(x^2) + eps)
+  with a per-channel scale gamma and the caller's eps.
 """
 from __future__ import annotations
 
@@ -148,18 +157,36 @@ def newton_schulz(g, iters=NS_ITERS, eps=NS_EPS):
     return x.T if tall else x
 
 
-def update_head(w1, w3, w2, k, v, eta, lr, steps):
+def norm_preserving_step(w, delta):
+    """W^ = ||W||_F * (W - Delta) / ||W - Delta||_F for one matrix ([ZipMap] 关键设计 3).
+
+    The step direction of W - Delta is kept and its Frobenius norm is reset to
+    that of W.  W - Delta = 0 gives the zero matrix.
+    """
+    moved = w - delta
+    n_moved = np.linalg.norm(moved)
+    if n_moved == 0:
+        return np.zeros_like(moved)
+    return moved * (np.linalg.norm(w) / n_moved)
+
+
+def update_head(w1, w3, w2, k, v, eta, lr, steps, norm_preserve=False):
     """One head's update: ``steps`` times G = grad, W <- W - lr * NS(G).
 
     [Scal3R] eq. (3) with the chunk-wise sum of 方案1; [ZipMap] 关键设计 1 and 3;
     [VGG-T3] 关键设计 3 (steps = 2 re-runs the same update at the new W).
+    ``norm_preserve`` replaces each matrix's plain step by
+    ``norm_preserving_step(W, lr * NS(G))``.
     Returns (W1^, W3^, W2^), the last step's (G1, G3, G2) and (NS(G1), NS(G3), NS(G2)).
     """
     g = ns = None
     for _ in range(steps):
         g = gradient(w1, w3, w2, k, v, eta)
         ns = tuple(newton_schulz(gj) for gj in g)
-        w1, w3, w2 = w1 - lr * ns[0], w3 - lr * ns[1], w2 - lr * ns[2]
+        if norm_preserve:
+            w1, w3, w2 = (norm_preserving_step(wj, lr * nj) for wj, nj in zip((w1, w3, w2), ns))
+        else:
+            w1, w3, w2 = w1 - lr * ns[0], w3 - lr * ns[1], w2 - lr * ns[2]
     return (w1, w3, w2), g, ns
 
 
@@ -175,7 +202,7 @@ def _head_cols(h, d):
     return slice(h * d, (h + 1) * d)
 
 
-def update(w1, w3, w2, k, v, eta, lr, steps):
+def update(w1, w3, w2, k, v, eta, lr, steps, norm_preserve=False):
     """Multi-head update.  w1, w3 [H, m, d]; w2 [H, d, m]; k, v [N, H*d]; eta [H, N].
 
     Returns (W^, G, NS) where each is a tuple (W1, W3, W2)-shaped stack over heads.
@@ -184,7 +211,7 @@ def update(w1, w3, w2, k, v, eta, lr, steps):
     outs, gs, nss = [], [], []
     for h in range(H):
         c = _head_cols(h, d)
-        wh, gh, nh = update_head(w1[h], w3[h], w2[h], k[:, c], v[:, c], eta[h], lr, steps)
+        wh, gh, nh = update_head(w1[h], w3[h], w2[h], k[:, c], v[:, c], eta[h], lr, steps, norm_preserve)
         outs.append(wh)
         gs.append(gh)
         nss.append(nh)
@@ -200,6 +227,19 @@ def apply(w1, w3, w2, q):
         c = _head_cols(h, d)
         out[:, c] = apply_head(w1[h], w3[h], w2[h], q[:, c])
     return out
+
+
+def rms_norm(x, gamma, eps):
+    """RMSNorm over each row: gamma * x / sqrt(mean(x^2) + eps) ([ZipMap] 关键设计 3)."""
+    return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps) * gamma
+
+
+def output_gate(o, wg, gamma, eps):
+    """o_i = RMSNorm(o'_i) * SiLU(W_g o'_i) for every row o'_i of ``o`` ([ZipMap] 关键设计 3).
+
+    o: [n, C]; wg: [C, C] (row = output channel); gamma: [C].
+    """
+    return rms_norm(o, gamma, eps) * silu(o @ wg.T)
 
 
 def shortconv2d(v, wconv, frames, tokens_per_frame, n_special, grid_h, grid_w):
@@ -244,7 +284,7 @@ def layer(w1, w3, w2, k, v, eta, q, lr, steps, conv=None):
     return apply(*w_hat, q), w_hat, g, ns
 
 
-def stream(w1, w3, w2, k, v, eta, q, lr, steps, chunk):
+def stream(w1, w3, w2, k, v, eta, q, lr, steps, chunk, norm_preserve=False):
     """Causal chunked processing ([ZipMap] 关键设计 4; [LoGeR] 方法概览).
 
     For each chunk c of ``chunk`` consecutive tokens: O_c = apply(W, Q_c), then
@@ -256,5 +296,5 @@ def stream(w1, w3, w2, k, v, eta, q, lr, steps, chunk):
     for t0 in range(0, n, chunk):
         t1 = min(n, t0 + chunk)
         out[t0:t1] = apply(*w, q[t0:t1])
-        w, _, _ = update(*w, k[t0:t1], v[t0:t1], eta[:, t0:t1], lr, steps)
+        w, _, _ = update(*w, k[t0:t1], v[t0:t1], eta[:, t0:t1], lr, steps, norm_preserve)
     return out, w

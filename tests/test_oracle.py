@@ -323,6 +323,91 @@ def test_shortconv2d_delta_and_box_closed_forms(rng):
     np.testing.assert_array_equal(got, np.array([[3, 4, 5], [6, 7, 8], [0, 0, 0]], float))
 
 
+# ------------------------------------------- ZipMap stabilisers (optional forms)
+def test_norm_preserving_step_hand_example():
+    # ||W|| = 5, W - Delta = diag(0, 4) with norm 4, so W^ = diag(0, 5)
+    w = np.array([[3.0, 0.0], [0.0, 4.0]])
+    delta = np.array([[3.0, 0.0], [0.0, 0.0]])
+    np.testing.assert_array_equal(oracle.norm_preserving_step(w, delta), np.array([[0.0, 0.0], [0.0, 5.0]]))
+    # W - Delta = 0 gives the zero matrix; Delta = 0 gives W back
+    assert np.all(oracle.norm_preserving_step(w, w) == 0.0)
+    np.testing.assert_allclose(oracle.norm_preserving_step(w, np.zeros_like(w)), w, rtol=1e-15)
+
+
+@pytest.mark.parametrize("steps", [1, 2])
+def test_norm_preserving_update_keeps_norms_and_plain_direction(rng, steps):
+    H, d, m = 2, 8, 16
+    w, k, v, q, eta = _layer_inputs(rng, H, d, m, 60, 10, scale=0.3)
+    lr = 0.2
+    w_np, g_np, ns_np = oracle.update(*w, k, v, eta, lr, steps, norm_preserve=True)
+    # the Frobenius norm of every matrix of every head is that of the input
+    for a, b in zip(w_np, w):
+        for h in range(H):
+            assert np.linalg.norm(a[h]) == pytest.approx(np.linalg.norm(b[h]), rel=1e-13)
+    # one step: the same direction as the plain step W - lr NS(G), positive factor
+    if steps == 1:
+        w_plain, g_pl, _ = oracle.update(*w, k, v, eta, lr, 1)
+        for a, b in zip(w_np, w_plain):
+            for h in range(H):
+                cos = np.sum(a[h] * b[h]) / (np.linalg.norm(a[h]) * np.linalg.norm(b[h]))
+                assert cos == pytest.approx(1.0, abs=1e-13)
+        for a, b in zip(g_np, g_pl):
+            assert np.array_equal(a, b)
+    # lr = 0 leaves W (to rounding)
+    w0, _, _ = oracle.update(*w, k, v, eta, 0.0, steps, norm_preserve=True)
+    for a, b in zip(w0, w):
+        np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-16)
+
+
+def test_norm_preserving_stream_equals_sequential_calls(rng):
+    w, k, v, q, eta = _layer_inputs(rng, 2, 8, 16, 50, 50, scale=0.3)
+    o, wf = oracle.stream(*w, k, v, eta, q, 0.1, 1, chunk=20, norm_preserve=True)
+    cur = w
+    for t0 in (0, 20, 40):
+        t1 = min(50, t0 + 20)
+        np.testing.assert_array_equal(o[t0:t1], oracle.apply(*cur, q[t0:t1]))
+        cur, _, _ = oracle.update(*cur, k[t0:t1], v[t0:t1], eta[:, t0:t1], 0.1, 1, norm_preserve=True)
+    for a, b in zip(wf, cur):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_output_gate_matches_library_rmsnorm_linear_silu(rng, eps):
+    # torch's rms_norm (eps inside the root, per-channel weight), linear (x W^T) and SiLU
+    n, C = 40, 24
+    o = rng.normal(0, 1.5, (n, C))
+    wg = rng.normal(0, 0.3, (C, C))
+    gamma = rng.uniform(0.5, 1.5, C)
+    got = oracle.output_gate(o, wg, gamma, eps)
+    t = torch.from_numpy
+    F = torch.nn.functional
+    ref = F.rms_norm(t(o), (C,), t(gamma), eps) * F.silu(F.linear(t(o), t(wg)))
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_output_gate_rank_one_and_degenerate_closed_forms(rng):
+    n, C = 6, 8
+    o = rng.normal(0, 1, (n, C))
+    gamma = np.ones(C)
+    # W_g = 0: SiLU(0) = 0 closes the gate
+    assert np.all(oracle.output_gate(o, np.zeros((C, C)), gamma, 1e-6) == 0.0)
+    # W_g = e_a e_b^T: only channel a is open, with gate SiLU(o'_b)
+    a, b = 5, 2
+    wg = np.zeros((C, C))
+    wg[a, b] = 1.0
+    got = oracle.output_gate(o, wg, gamma, 0.0)
+    others = [c for c in range(C) if c != a]
+    assert np.all(got[:, others] == 0.0)
+    for i in range(n):
+        rms = math.sqrt(sum(x * x for x in o[i]) / C)
+        silu_b = o[i, b] / (1.0 + math.exp(-o[i, b]))
+        assert got[i, a] == pytest.approx(o[i, a] / rms * silu_b, rel=1e-13)
+    # scale invariance of the norm (eps = 0): o -> 3 o with W_g -> W_g / 3 is unchanged
+    wg = rng.normal(0, 0.5, (C, C))
+    np.testing.assert_allclose(oracle.output_gate(3 * o, wg / 3, gamma, 0.0),
+                               oracle.output_gate(o, wg, gamma, 0.0), rtol=1e-13, atol=1e-15)
+
+
 # ------------------------------------------------------- oracle's own rounding
 def test_fp32_oracle_within_1e5_of_fp64(rng):
     H, d, m, n = 2, 64, 128, 3000
