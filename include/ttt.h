@@ -109,6 +109,29 @@ int ttt_update(int32_t heads, int32_t d, int32_t m,
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ttt_update_ex -- ttt_update with option flags (ttt_update is flags = 0).
+ *
+ * TTT_NORM_PRESERVE: [ZipMap] 关键设计 3's norm-preserving step.  Each step
+ *   replaces W <- W - lr * NS(G) by
+ *     W <- ||W||_F * (W - lr * NS(G)) / ||W - lr * NS(G)||_F
+ *   for every weight matrix of every head separately (Frobenius norms, ||W||
+ *   taken before the step; lr = 1 is the page's form with Delta = NS(g)).  If
+ *   W - lr * NS(G) is exactly zero the matrix becomes zero.  The norms are fp32
+ *   sums of squares in a fixed order, so results stay deterministic.
+ * Other bits are reserved: TTT_EINVAL.  Every other argument is as in ttt_update;
+ * the workspace size is the same.
+ */
+enum { TTT_NORM_PRESERVE = 1 };
+int ttt_update_ex(int32_t heads, int32_t d, int32_t m,
+                  const float *w1, const float *w3, const float *w2,
+                  float *w1_out, float *w3_out, float *w2_out,
+                  const void *k, const void *v, int64_t ld_kv,
+                  const float *eta, int64_t eta_head_stride,
+                  int64_t n, float lr, int32_t steps, int32_t dtype, uint32_t flags,
+                  float *grad_out, float *ns_out,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ttt_apply -- o_i = f_W(q_i) for every row ([Scal3R] eq. (4); [ZipMap]
  * 关键设计 1; [tttLRM] query-only tokens use the same call).
  *
@@ -140,6 +163,27 @@ int ttt_shortconv2d(const void *v, void *v_out, int64_t ld, const float *wconv,
                     int32_t grid_h, int32_t grid_w, int32_t channels,
                     int32_t dtype, void *stream);
 
+/*
+ * ttt_output_gate -- [ZipMap] 关键设计 3's gated output unit, applied to the
+ * output rows o'_i of ttt_apply:
+ *   o_i = RMSNorm(o'_i) * SiLU(W_g o'_i),
+ *   RMSNorm(x)[c] = gamma[c] * x[c] / sqrt(mean_c'(x[c']^2) + eps),
+ *   (W_g x)[c]    = sum_c' wg[c][c'] * x[c'],   SiLU(z) = z / (1 + e^-z).
+ * A row is the whole C = `channels` wide output (all heads), the mean runs over
+ * those C channels, and there is no bias.
+ *
+ * o_in, o_out : [n][ld_in] / [n][ld_out] device rows, `dtype`, columns [0, C)
+ *               used; must not overlap each other or wg.
+ * wg          : [C][C] row-major, `dtype`, device, 16-byte aligned.
+ * gamma       : [C] fp32, device.
+ * eps         : >= 0, finite.
+ * Requires C >= 64, C % 64 == 0, C <= ld_in, C <= ld_out, and the row
+ * alignment of the conventions above.  n = 0 launches nothing.  The products
+ * accumulate in fp32 (bf16 or fp32 MFMA operands, as `dtype`).
+ */
+int ttt_output_gate(int32_t channels, const void *o_in, int64_t ld_in, const void *wg, const float *gamma,
+                    float eps, void *o_out, int64_t ld_out, int64_t n, int32_t dtype, void *stream);
+
 /* Bytes of workspace ttt_stream needs for chunks of `chunk` tokens. */
 int ttt_stream_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t chunk,
                                int32_t dtype, size_t *bytes);
@@ -159,6 +203,15 @@ int ttt_stream(int32_t heads, int32_t d, int32_t m,
                const void *q, int64_t ld_q, void *o, int64_t ld_o,
                int64_t n, int64_t chunk, float lr, int32_t steps, int32_t dtype,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/* ttt_stream with the flags of ttt_update_ex applied to every chunk's update. */
+int ttt_stream_ex(int32_t heads, int32_t d, int32_t m,
+                  float *w1, float *w3, float *w2,
+                  const void *k, const void *v, int64_t ld_kv,
+                  const float *eta, int64_t eta_head_stride,
+                  const void *q, int64_t ld_q, void *o, int64_t ld_o,
+                  int64_t n, int64_t chunk, float lr, int32_t steps, int32_t dtype, uint32_t flags,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Process-wide tuning / testing switches.
@@ -184,7 +237,7 @@ int ttt_set_option(int32_t option, int64_t value);
  */
 typedef enum {
   TTT_K_CONV = 0, TTT_K_CAST = 1, TTT_K_GRAD = 2, TTT_K_REDUCE = 3,
-  TTT_K_NS = 4, TTT_K_APPLY = 5, TTT_K_COUNT = 6
+  TTT_K_NS = 4, TTT_K_APPLY = 5, TTT_K_GATE = 6, TTT_K_COUNT = 7
 } ttt_kernel_kind;
 int ttt_profile_enable(int32_t on);
 int ttt_profile_reset(void);

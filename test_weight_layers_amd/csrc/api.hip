@@ -120,7 +120,8 @@ struct UpdatePlan {
   bool bf16, fast, xcd;
   int dchunks, splits, grid;
   int64_t n, nblk;
-  size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_xt0, off_xt1, off_a, off_b, off_sync, total;
+  size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_xt0, off_xt1, off_a, off_b, off_sync, off_wsq;
+  size_t total;
 };
 
 UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
@@ -166,6 +167,8 @@ UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
   off = align256(off + (size_t)3 * H * p.r * p.r * 4);
   p.off_sync = off;
   off = align256(off + (size_t)H * p.splits * 4);
+  p.off_wsq = off;                                   // norm-preserving step: 2 x [3H][d*m/4096]
+  off = align256(off + 2 * (3 * mat / 4096) * 4);
   p.total = off;
   return p;
 }
@@ -189,9 +192,10 @@ constexpr float kNsEps = 1e-7f;
 // ops_ready: the operand copies of `in` are already at the start of the workspace
 // (written by the previous call's last step or by an apply cast of the same layout).
 // keep_ops: the last step leaves the operand copies of `out` there.
+// norm: the norm-preserving step (W^ = ||W|| (W - lr NS) / ||W - lr NS|| per matrix).
 int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v, int64_t ld, const float *eta,
               int64_t eta_hs, float lr, int steps, float *grad_out, float *ns_out, char *ws, hipStream_t s,
-              bool ops_ready = false, bool keep_ops = false) {
+              bool norm, bool ops_ready = false, bool keep_ops = false) {
   const bool fused = !g_ns_unfused;
   const size_t mat = (size_t)P.H * P.d * P.m;
   void *const wop = ws + P.off_wop;
@@ -202,6 +206,8 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
   float *x1 = reinterpret_cast<float *>(ws + P.off_x1);
   float *am = reinterpret_cast<float *>(ws + P.off_a);
   float *bm = reinterpret_cast<float *>(ws + P.off_b);
+  float *wsq = reinterpret_cast<float *>(ws + P.off_wsq);
+  const int slots = P.d * P.m / 4096;
   const NsShape sh{P.H, P.d, P.m};
   int st;
   for (int t = 0; t < steps; ++t) {
@@ -261,8 +267,16 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
       }
       np.lr = lr, np.eps = kNsEps, np.a_coef = kNsA, np.b_coef = kNsB, np.c_coef = kNsC;
       np.iters = kNsIters, np.heads = P.H, np.d = P.d, np.m = P.m, np.r = P.r, np.c = P.c;
+      np.norm_preserve = norm, np.wsq = wsq;
       st = run(TTT_K_NS, "newton_schulz", s, [&] { return launch_ns_optimiser(np, P.bf16, s); });
       if (st) return st;
+      if (norm) {
+        st = run(TTT_K_NS, "norm_rescale", s, [&] {
+          return launch_norm_rescale(out.w1, out.w3, out.w2, wsq, slots, np.op1v, np.op3v, np.op2tv, P.H, P.d, P.m,
+                                     P.bf16, s);
+        });
+        if (st) return st;
+      }
       continue;
     }
     st = run(TTT_K_REDUCE, "reduce", s, [&] {
@@ -288,10 +302,26 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
       x = xn;
       xn = tmp;
     }
+    if (norm) {
+      st = run(TTT_K_NS, "weight_sumsq", s, [&] { return launch_weight_sumsq(src.w1, src.w3, src.w2, wsq, P.H, P.d,
+                                                                              P.m, s); });
+      if (st) return st;
+    }
     st = run(TTT_K_NS, "ns_step", s, [&] {
       return launch_ns_step(x, src.w1, src.w3, src.w2, out.w1, out.w3, out.w2, last ? ns_out : nullptr, lr, sh, s);
     });
     if (st) return st;
+    if (norm) {
+      st = run(TTT_K_NS, "weight_sumsq", s, [&] {
+        return launch_weight_sumsq(out.w1, out.w3, out.w2, wsq + 3 * P.H * slots, P.H, P.d, P.m, s);
+      });
+      if (st) return st;
+      st = run(TTT_K_NS, "norm_rescale", s, [&] {
+        return launch_norm_rescale(out.w1, out.w3, out.w2, wsq, slots, nullptr, nullptr, nullptr, P.H, P.d, P.m,
+                                   P.bf16, s);
+      });
+      if (st) return st;
+    }
   }
   return TTT_OK;
 }
@@ -375,12 +405,14 @@ int ttt_stream_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t chun
   return TTT_OK;
 }
 
-int ttt_update(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2, float *w1_out,
-               float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv, const float *eta,
-               int64_t eta_head_stride, int64_t n, float lr, int32_t steps, int32_t dtype, float *grad_out,
-               float *ns_out, void *workspace, size_t workspace_bytes, void *stream) {
+int ttt_update_ex(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2,
+                  float *w1_out, float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv,
+                  const float *eta, int64_t eta_head_stride, int64_t n, float lr, int32_t steps, int32_t dtype,
+                  uint32_t flags, float *grad_out, float *ns_out, void *workspace, size_t workspace_bytes,
+                  void *stream) {
   int st = check_shape(heads, d, m, dtype);
   if (st) return st;
+  if (flags & ~uint32_t(TTT_NORM_PRESERVE)) return fail(TTT_EINVAL, "unknown flag bits 0x%x", flags);
   if ((st = check_weights(w1, w3, w2))) return st;
   if (!w1_out || !w3_out || !w2_out) return fail(TTT_EINVAL, "output fast-weight pointer is null");
   const size_t wb = (size_t)heads * d * m * 4;
@@ -403,7 +435,16 @@ int ttt_update(int32_t heads, int32_t d, int32_t m, const float *w1, const float
   const UpdatePlan P = plan_update(heads, d, m, n, dtype);
   if ((st = check_ws(workspace, workspace_bytes, P.total))) return st;
   return do_update(P, W3{w1, w3, w2}, W3o{w1_out, w3_out, w2_out}, k, v, ld_kv, eta, eta_head_stride, lr, steps,
-                   grad_out, ns_out, static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+                   grad_out, ns_out, static_cast<char *>(workspace), static_cast<hipStream_t>(stream),
+                   (flags & TTT_NORM_PRESERVE) != 0);
+}
+
+int ttt_update(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2, float *w1_out,
+               float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv, const float *eta,
+               int64_t eta_head_stride, int64_t n, float lr, int32_t steps, int32_t dtype, float *grad_out,
+               float *ns_out, void *workspace, size_t workspace_bytes, void *stream) {
+  return ttt_update_ex(heads, d, m, w1, w3, w2, w1_out, w3_out, w2_out, k, v, ld_kv, eta, eta_head_stride, n, lr,
+                       steps, dtype, 0u, grad_out, ns_out, workspace, workspace_bytes, stream);
 }
 
 int ttt_apply(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2, const void *q,
@@ -448,12 +489,38 @@ int ttt_shortconv2d(const void *v, void *v_out, int64_t ld, const float *wconv, 
   });
 }
 
-int ttt_stream(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float *w2, const void *k, const void *v,
-               int64_t ld_kv, const float *eta, int64_t eta_head_stride, const void *q, int64_t ld_q, void *o,
-               int64_t ld_o, int64_t n, int64_t chunk, float lr, int32_t steps, int32_t dtype, void *workspace,
-               size_t workspace_bytes, void *stream) {
+int ttt_output_gate(int32_t channels, const void *o_in, int64_t ld_in, const void *wg, const float *gamma,
+                    float eps, void *o_out, int64_t ld_out, int64_t n, int32_t dtype, void *stream) {
+  if (dtype != TTT_F32 && dtype != TTT_BF16) return fail(TTT_EUNSUPPORTED, "unknown dtype %d", dtype);
+  if (channels < 64 || channels % 64 != 0) return fail(TTT_EUNSUPPORTED, "channels must be a positive multiple of 64");
+  if (n < 0) return fail(TTT_EINVAL, "n must be >= 0");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(TTT_EINVAL, "eps must be finite and >= 0");
+  if (n == 0) return TTT_OK;
+  int st;
+  if ((st = check_rows(o_in, ld_in, 1, channels, dtype, "o_in"))) return st;
+  if ((st = check_rows(o_out, ld_out, 1, channels, dtype, "o_out"))) return st;
+  if (!wg || reinterpret_cast<uintptr_t>(wg) % 16 != 0) return fail(TTT_EINVAL, "wg is null or not 16-byte aligned");
+  if (!gamma) return fail(TTT_EINVAL, "gamma is null");
+  const size_t es = esize(dtype);
+  const size_t in_b = (size_t)n * ld_in * es, out_b = (size_t)n * ld_out * es, wg_b = (size_t)channels * channels * es;
+  if (overlap(o_in, in_b, o_out, out_b)) return fail(TTT_EINVAL, "o_in and o_out must not overlap");
+  if (overlap(wg, wg_b, o_out, out_b)) return fail(TTT_EINVAL, "wg and o_out must not overlap");
+  GateParams gp{};
+  gp.o_in = o_in, gp.ld_in = ld_in, gp.wg = wg, gp.gamma = gamma, gp.eps = eps;
+  gp.o_out = o_out, gp.ld_out = ld_out, gp.n = n, gp.channels = channels, gp.tiles_n = gate_tiles(n);
+  const int64_t blocks = (gp.tiles_n * ((channels + 127) / 128) + 7) / 8 * 8;
+  if (blocks > 0x7fffffffLL) return fail(TTT_EUNSUPPORTED, "n too large for one launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run(TTT_K_GATE, "output_gate", s, [&] { return launch_gate(gp, dtype == TTT_BF16, s); });
+}
+
+int ttt_stream_ex(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float *w2, const void *k,
+                  const void *v, int64_t ld_kv, const float *eta, int64_t eta_head_stride, const void *q, int64_t ld_q,
+                  void *o, int64_t ld_o, int64_t n, int64_t chunk, float lr, int32_t steps, int32_t dtype,
+                  uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
   int st = check_shape(heads, d, m, dtype);
   if (st) return st;
+  if (flags & ~uint32_t(TTT_NORM_PRESERVE)) return fail(TTT_EINVAL, "unknown flag bits 0x%x", flags);
   if ((st = check_weights(w1, w3, w2))) return st;
   if (n < 0 || chunk < 1 || steps < 1) return fail(TTT_EINVAL, "need n >= 0, chunk >= 1, steps >= 1");
   if (!std::isfinite(lr)) return fail(TTT_EINVAL, "lr must be finite");
@@ -487,10 +554,18 @@ int ttt_stream(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float 
     const bool ready = shared || (carry && dtype == TTT_F32 && !first);
     st = do_update(P, W3{w1, w3, w2}, W3o{w1, w3, w2}, static_cast<const char *>(k) + t0 * ld_kv * es,
                    static_cast<const char *>(v) + t0 * ld_kv * es, ld_kv, eta + t0, eta_head_stride, lr, steps,
-                   nullptr, nullptr, ws, s, ready, carry);
+                   nullptr, nullptr, ws, s, (flags & TTT_NORM_PRESERVE) != 0, ready, carry);
     if (st) return st;
   }
   return TTT_OK;
+}
+
+int ttt_stream(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float *w2, const void *k, const void *v,
+               int64_t ld_kv, const float *eta, int64_t eta_head_stride, const void *q, int64_t ld_q, void *o,
+               int64_t ld_o, int64_t n, int64_t chunk, float lr, int32_t steps, int32_t dtype, void *workspace,
+               size_t workspace_bytes, void *stream) {
+  return ttt_stream_ex(heads, d, m, w1, w3, w2, k, v, ld_kv, eta, eta_head_stride, q, ld_q, o, ld_o, n, chunk, lr,
+                       steps, dtype, 0u, workspace, workspace_bytes, stream);
 }
 
 int ttt_set_option(int32_t option, int64_t value) {

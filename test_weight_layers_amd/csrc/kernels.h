@@ -96,8 +96,41 @@ struct NsStepParams {
   void *op1v, *op3v, *op2tv;
   float lr, eps, a_coef, b_coef, c_coef;
   int iters, heads, d, m, r, c;
+  // Norm-preserving form: the last product writes the unscaled W - lr NS(G) and
+  // per-tile sums of squares of W and of that result into wsq (layout of
+  // launch_norm_rescale, (d/64)(m/64) slots per matrix) instead of operand copies.
+  int norm_preserve;
+  float *wsq;
 };
 hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s);
+
+// Per-4096-element sums of squares of W1, W3, W2 in matrix order [3][H] (d*m/4096
+// slots per matrix), written to out[0 .. 3H * slots).
+hipError_t launch_weight_sumsq(const float *w1, const float *w3, const float *w2, float *out, int heads, int d,
+                               int m, hipStream_t s);
+// Norm-preserving rescale of each matrix b of W_out ([3][H] order):
+//   W_out <- W_out * sqrt(sum wsq[b*slots ..]) / sqrt(sum wsq[(3H + b)*slots ..])
+// (zero when the second sum is zero), then the operand copies op1, op3 ([H][m][d])
+// and op2t (W2^T, [H][m][d]) of the result, each when non-null.
+hipError_t launch_norm_rescale(float *w1o, float *w3o, float *w2o, const float *wsq, int slots, void *op1,
+                               void *op3, void *op2t, int heads, int d, int m, bool bf16, hipStream_t s);
+
+// Gated output o = gamma * o' / sqrt(mean(o'^2) + eps) * SiLU(W_g o') over rows of
+// `channels` elements (channels % 64 == 0); W_g is [channels][channels], row = output.
+struct GateParams {
+  const void *o_in;
+  int64_t ld_in;
+  const void *wg;
+  const float *gamma;
+  float eps;
+  void *o_out;
+  int64_t ld_out;
+  int64_t n;
+  int channels;
+  int64_t tiles_n;           // gate_tiles(n)
+};
+int64_t gate_tiles(int64_t n);
+hipError_t launch_gate(const GateParams &p, bool bf16, hipStream_t s);
 
 hipError_t launch_conv(const void *v, void *out, int64_t ld, const float *w, int frames, int tpf,
                        int nsp, int gh, int gw, int channels, bool bf16, hipStream_t s);

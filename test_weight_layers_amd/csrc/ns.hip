@@ -347,6 +347,7 @@ __global__ __launch_bounds__(256) void ns_tile_kernel(NsStepParams p, int cur, i
   if (PH >= 2) tile_nt(Bm + (int64_t)ti * kT * r, r, XT + (int64_t)tj * kT * r, r, r, sm, acc);
   const int hj = b / H, h = b % H;
   const bool tr = (hj < 2 ? m : d) > (hj < 2 ? d : m);
+  float ssw = 0.0f, ssd = 0.0f;      // norm-preserving form: sums of squares of W and W - lr NS
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -378,13 +379,16 @@ __global__ __launch_bounds__(256) void ns_tile_kernel(NsStepParams p, int cur, i
           const float *W = hj == 0 ? p.w1 : (hj == 1 ? p.w3 : p.w2);
           float *Wo = hj == 0 ? p.w1o : (hj == 1 ? p.w3o : p.w2o);
           const int gcols = hj < 2 ? d : m;
-          T *op = static_cast<T *>(hj == 0 ? p.op1v : (hj == 1 ? p.op3v : p.op2tv));
+          T *op = p.norm_preserve ? nullptr : static_cast<T *>(hj == 0 ? p.op1v : (hj == 1 ? p.op3v : p.op2tv));
 #pragma unroll
           for (int z = 0; z < 4; ++z) {
             const int gr = tr ? jj : i + z, gc = tr ? i + z : jj;
             const int64_t ew = (int64_t)h * mat + (int64_t)gr * gcols + gc;
-            const float nw = W[ew] - p.lr * v[z];
+            const float w0 = W[ew];
+            const float nw = w0 - p.lr * v[z];
             Wo[ew] = nw;
+            ssw += w0 * w0;
+            ssd += nw * nw;
             if (p.ns_out) p.ns_out[(int64_t)b * mat + (int64_t)gr * gcols + gc] = v[z];
             if (op) {
               // W1/W3 copies keep G's [m][d] layout; W2 [d][m] is copied transposed
@@ -395,6 +399,98 @@ __global__ __launch_bounds__(256) void ns_tile_kernel(NsStepParams p, int cur, i
         }
       }
     }
+  if (PH == 3 && p.norm_preserve) {
+    const float sw = block_sum(ssw, sm), sd = block_sum(ssd, sm);
+    if (t == 0) {
+      p.wsq[tile] = sw;
+      p.wsq[(int64_t)gridDim.x + tile] = sd;
+    }
+  }
+}
+
+// ---------------------------------------------------- norm-preserving step
+// ZipMap 关键设计 3 keeps the Frobenius norm of each fast-weight matrix across the
+// step: W^ = ||W|| (W - Delta) / ||W - Delta||.  The step kernels leave W - Delta
+// in W_out and per-tile sums of squares of W and of W - Delta; the rescale sums
+// them in fixed order (the same in every workgroup) and scales W_out in place.
+
+__global__ __launch_bounds__(256) void weight_sumsq_kernel(const float *__restrict__ w1, const float *__restrict__ w3,
+                                                           const float *__restrict__ w2, float *__restrict__ out,
+                                                           int heads, int64_t mat) {
+  __shared__ NsSmem sm;
+  const int64_t e0 = (int64_t)blockIdx.x * kRedBlock;
+  const int64_t b = e0 / mat;
+  const int j = (int)(b / heads), h = (int)(b % heads);
+  const float *src = (j == 0 ? w1 : (j == 1 ? w3 : w2)) + (int64_t)h * mat + (e0 - b * mat);
+  float ss = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(src + (q * 256 + threadIdx.x) * 4);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  const float tot = block_sum(ss, sm);
+  if (threadIdx.x == 0) out[blockIdx.x] = tot;
+}
+
+// One 64x64 tile of matrix b in W's own layout per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void norm_rescale_kernel(float *w1o, float *w3o, float *w2o,
+                                                           const float *__restrict__ wsq, int slots, T *op1, T *op3,
+                                                           T *op2t, int heads, int d, int m) {
+  __shared__ NsSmem sm;
+  const int t = threadIdx.x;
+  const int64_t mat = (int64_t)d * m;
+  const int tiles = (int)(mat / (kT * kT));
+  const int b = blockIdx.x / tiles, tt = blockIdx.x % tiles;
+  const int j = b / heads, h = b % heads;
+  const int B = 3 * heads;
+  float sw = 0.0f, sd = 0.0f;
+  for (int i = t; i < slots; i += 256) {
+    sw += wsq[(int64_t)b * slots + i];
+    sd += wsq[(int64_t)(B + b) * slots + i];
+  }
+  sw = block_sum(sw, sm);
+  sd = block_sum(sd, sm);
+  const float scale = sd > 0.0f ? sqrtf(sw) / sqrtf(sd) : 0.0f;
+  const int rows = j < 2 ? m : d, cols = j < 2 ? d : m;
+  const int ct = cols / kT;
+  const int r0 = (tt / ct) * kT, c0 = (tt % ct) * kT;
+  float *W = (j == 0 ? w1o : (j == 1 ? w3o : w2o)) + (int64_t)h * mat;
+  T *op = j == 0 ? op1 : (j == 1 ? op3 : nullptr);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = t + 256 * u, rr = q >> 4, cc = (q & 15) * 4;
+    f32x4 *pw = reinterpret_cast<f32x4 *>(W + (int64_t)(r0 + rr) * cols + c0 + cc);
+    const f32x4 v = *pw * scale;
+    *pw = v;
+    if (op) {
+#pragma unroll
+      for (int z = 0; z < 4; ++z) op[(int64_t)h * mat + (int64_t)(r0 + rr) * cols + c0 + cc + z] = from_f32<T>(v[z]);
+    }
+    if (j == 2) {
+#pragma unroll
+      for (int z = 0; z < 4; ++z) sm.tr[rr][cc + z] = v[z];
+    }
+  }
+  if (j == 2 && op2t) {               // W2 [d][m] tile -> W2^T [m][d]
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = t + 256 * u, rr = q >> 4, cc = (q & 15) * 4;
+#pragma unroll
+      for (int z = 0; z < 4; ++z)
+        op2t[(int64_t)h * mat + (int64_t)(c0 + rr) * d + r0 + cc + z] = from_f32<T>(sm.tr[cc + z][rr]);
+    }
+  }
+}
+
+template <typename T>
+hipError_t rescale_impl(float *w1o, float *w3o, float *w2o, const float *wsq, int slots, void *op1, void *op3,
+                        void *op2t, int heads, int d, int m, hipStream_t s) {
+  const int blocks = 3 * heads * (d / kT) * (m / kT);
+  hipLaunchKernelGGL(norm_rescale_kernel<T>, dim3(blocks), dim3(256), 0, s, w1o, w3o, w2o, wsq, slots,
+                     static_cast<T *>(op1), static_cast<T *>(op3), static_cast<T *>(op2t), heads, d, m);
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -418,6 +514,20 @@ hipError_t ns_optimiser_impl(const NsStepParams &p, hipStream_t s) {
 
 hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s) {
   return bf16 ? ns_optimiser_impl<__bf16>(p, s) : ns_optimiser_impl<float>(p, s);
+}
+
+hipError_t launch_weight_sumsq(const float *w1, const float *w3, const float *w2, float *out, int heads, int d,
+                               int m, hipStream_t s) {
+  const int64_t mat = (int64_t)d * m;
+  hipLaunchKernelGGL(weight_sumsq_kernel, dim3((unsigned)(3 * heads * mat / kRedBlock)), dim3(256), 0, s, w1, w3, w2,
+                     out, heads, mat);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_rescale(float *w1o, float *w3o, float *w2o, const float *wsq, int slots, void *op1,
+                               void *op3, void *op2t, int heads, int d, int m, bool bf16, hipStream_t s) {
+  return bf16 ? rescale_impl<__bf16>(w1o, w3o, w2o, wsq, slots, op1, op3, op2t, heads, d, m, s)
+              : rescale_impl<float>(w1o, w3o, w2o, wsq, slots, op1, op3, op2t, heads, d, m, s);
 }
 
 hipError_t launch_cast(const float *w1, const float *w3, const float *w2, void *w1o, void *w3o, void *w2to,

@@ -10,6 +10,9 @@ arithmetic.  Recipe (per workload in ``configs.py``):
   max(||x||, 1e-12) -- the parameter-free normalisation that replaces LayerNorm
   on Q/K (VGG-T3, 关键设计 1).  Then rounded to nearest-even into the token dtype.
 * Per-token learning rates eta in [H, N], fp32, U[0, 0.1).
+* Gated-output unit: input rows o' [rows, C] N(0, 1) in the token dtype; gate
+  matrix W_g [C, C] N(0, 1/C) (unit-variance pre-activations) in the token dtype;
+  RMSNorm scale gamma [C] fp32, U[0.5, 1.5).
 
 Every tensor is drawn in row blocks of ``ROW_BLOCK`` tokens, block b of stream s
 from ``SeedSequence(seed, spawn_key=(s, b))`` (PCG64), so any N-prefix of a
@@ -28,7 +31,7 @@ import torch
 from .configs import LayerConfig
 
 ROW_BLOCK = 16384
-STREAMS = ("w", "conv", "k", "v", "q", "q_extra", "eta")
+STREAMS = ("w", "conv", "k", "v", "q", "q_extra", "eta", "gate_in", "gate_w")
 TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
@@ -95,6 +98,19 @@ def conv_weights(seed: int, channels: int) -> torch.Tensor:
     """[channels, 3, 3] fp32 depthwise taps, N(0, 0.1)."""
     g = _rng(seed, "conv", 0)
     return torch.from_numpy(g.standard_normal((channels, 3, 3), dtype=np.float32) * np.float32(0.1))
+
+
+def gate_weights(seed: int, channels: int, dtype: torch.dtype):
+    """(W_g [C, C] in `dtype`, N(0, 1/C); gamma [C] fp32, U[0.5, 1.5))."""
+    g = _rng(seed, "gate_w", 0)
+    wg = g.standard_normal((channels, channels), dtype=np.float32) * np.float32(channels ** -0.5)
+    gamma = np.float32(0.5) + g.random(channels, dtype=np.float32)
+    return torch.from_numpy(wg).to(dtype), torch.from_numpy(gamma)
+
+
+def gate_rows(seed: int, rows: int, channels: int, dtype: torch.dtype) -> torch.Tensor:
+    """[rows, C] N(0, 1) input rows o' of the gated-output unit."""
+    return token_rows(seed, "gate_in", rows, 1, channels, False, dtype)
 
 
 @dataclass

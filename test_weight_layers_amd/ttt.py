@@ -19,10 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libttt.so")
 
 TTT_F32, TTT_BF16 = 0, 1
 OPT_FORCE_GENERAL, OPT_SPLITS, OPT_NS_UNFUSED = 0, 1, 2
-KERNEL_KINDS = ("conv", "cast", "grad", "reduce", "ns", "apply")
+KERNEL_KINDS = ("conv", "cast", "grad", "reduce", "ns", "apply", "gate")
+NORM_PRESERVE = 1
 EXPORTS = ("ttt_last_error", "ttt_update_workspace_bytes", "ttt_apply_workspace_bytes", "ttt_update",
-           "ttt_apply", "ttt_shortconv2d", "ttt_stream_workspace_bytes", "ttt_stream", "ttt_set_option",
-           "ttt_profile_enable", "ttt_profile_reset", "ttt_profile_read")
+           "ttt_update_ex", "ttt_apply", "ttt_output_gate", "ttt_shortconv2d", "ttt_stream_workspace_bytes",
+           "ttt_stream", "ttt_stream_ex", "ttt_set_option", "ttt_profile_enable", "ttt_profile_reset",
+           "ttt_profile_read")
 
 _lib = None
 
@@ -40,7 +42,7 @@ def load() -> ctypes.CDLL:
         raise TTTError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    vp, szp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+    vp, szp, u32 = ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_uint32
     sig = {
         "ttt_last_error": (ctypes.c_char_p, []),
         "ttt_update_workspace_bytes": (ctypes.c_int, [i32, i32, i32, i64, i32, szp]),
@@ -48,6 +50,11 @@ def load() -> ctypes.CDLL:
         "ttt_stream_workspace_bytes": (ctypes.c_int, [i32, i32, i32, i64, i32, szp]),
         "ttt_update": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, f32, i32,
                                       i32, vp, vp, vp, sz, vp]),
+        "ttt_update_ex": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, f32,
+                                         i32, i32, u32, vp, vp, vp, sz, vp]),
+        "ttt_output_gate": (ctypes.c_int, [i32, vp, i64, vp, vp, f32, vp, i64, i64, i32, vp]),
+        "ttt_stream_ex": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, i64, vp, i64, i64,
+                                         i64, f32, i32, i32, u32, vp, sz, vp]),
         "ttt_apply": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, i64, vp, i64, i64, i32, vp, sz, vp]),
         "ttt_shortconv2d": (ctypes.c_int, [vp, vp, i64, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
         "ttt_stream": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, i64, vp, i64, i64, i64,
@@ -131,8 +138,12 @@ def apply_workspace_bytes(heads: int, d: int, m: int, nq: int, dtype: torch.dtyp
 
 def update(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor, lr: float,
            steps: int = 1, out: Optional[Sequence[torch.Tensor]] = None, grad_out: Optional[torch.Tensor] = None,
-           ns_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Fast-weight update; returns (W1^, W3^, W2^).  ``out`` may be ``w`` (in place)."""
+           ns_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           norm_preserve: bool = False):
+    """Fast-weight update; returns (W1^, W3^, W2^).  ``out`` may be ``w`` (in place).
+
+    ``norm_preserve`` selects the norm-preserving step (flag TTT_NORM_PRESERVE).
+    """
     H, d, m = _weights(w)
     if out is None:
         out = tuple(torch.empty_like(x) for x in w)
@@ -158,9 +169,11 @@ def update(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: tor
     need = update_workspace_bytes(H, d, m, n, k.dtype)
     if workspace is None:
         workspace = _workspace(need, k.device)
-    _check(load().ttt_update(H, d, m, *map(_ptr, w), *map(_ptr, out), k.data_ptr(), v.data_ptr(), ld,
-                             eta.data_ptr(), ehs, n, float(lr), int(steps), code, _ptr(grad_out), _ptr(ns_out),
-                             _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream()))
+    flags = NORM_PRESERVE if norm_preserve else 0
+    _check(load().ttt_update_ex(H, d, m, *map(_ptr, w), *map(_ptr, out), k.data_ptr(), v.data_ptr(), ld,
+                                eta.data_ptr(), ehs, n, float(lr), int(steps), code, flags, _ptr(grad_out),
+                                _ptr(ns_out), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                _stream()))
     return tuple(out)
 
 
@@ -207,7 +220,7 @@ def stream_workspace_bytes(heads: int, d: int, m: int, chunk: int, dtype: torch.
 
 def stream(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor, q: torch.Tensor,
            lr: float, steps: int, chunk: int, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, norm_preserve: bool = False) -> torch.Tensor:
     """Chunked causal pass: per chunk apply then update; ``w`` is updated in place."""
     H, d, m = _weights(w)
     code = _dtype_code(k)
@@ -223,9 +236,28 @@ def stream(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: tor
     need = stream_workspace_bytes(H, d, m, chunk, k.dtype)
     if workspace is None:
         workspace = _workspace(need, k.device)
-    _check(load().ttt_stream(H, d, m, *map(_ptr, w), k.data_ptr(), v.data_ptr(), ld, eta.data_ptr(), ehs,
-                             q.data_ptr(), ldq, out.data_ptr(), ldo, n, chunk, float(lr), int(steps), code,
-                             _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream()))
+    flags = NORM_PRESERVE if norm_preserve else 0
+    _check(load().ttt_stream_ex(H, d, m, *map(_ptr, w), k.data_ptr(), v.data_ptr(), ld, eta.data_ptr(), ehs,
+                                q.data_ptr(), ldq, out.data_ptr(), ldo, n, chunk, float(lr), int(steps), code, flags,
+                                _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream()))
+    return out
+
+
+def output_gate(o: torch.Tensor, wg: torch.Tensor, gamma: torch.Tensor, eps: float,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """o_i = RMSNorm(o'_i) * SiLU(W_g o'_i) over rows of C = wg.shape[0] channels."""
+    code = _dtype_code(o)
+    C = wg.shape[0]
+    if wg.dtype != o.dtype or tuple(wg.shape) != (C, C) or not wg.is_contiguous() or not wg.is_cuda:
+        raise ValueError("wg must be a contiguous [C, C] GPU tensor of o's dtype")
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (C,) or not gamma.is_contiguous() or not gamma.is_cuda:
+        raise ValueError("gamma must be a contiguous float32 [C] GPU tensor")
+    ldi = _rows(o, "o")
+    if out is None:
+        out = torch.empty((o.shape[0], C), dtype=o.dtype, device=o.device)
+    ldo = _rows(out, "out")
+    _check(load().ttt_output_gate(C, o.data_ptr(), ldi, wg.data_ptr(), gamma.data_ptr(), float(eps), out.data_ptr(),
+                                  ldo, o.shape[0], code, _stream()))
     return out
 
 

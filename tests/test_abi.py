@@ -103,3 +103,27 @@ def test_apply_and_conv_argument_errors(lib):
     assert st == -2
     st = lib.ttt_set_option(9, 1)
     assert st == -1
+
+
+def test_update_ex_stream_ex_and_gate_argument_errors(lib):
+    fake = 1 << 20   # never dereferenced: every check below fails first
+    # unknown flag bits
+    st = lib.ttt_update_ex(1, 64, 128, fake, fake * 2, fake * 3, fake * 4, fake * 5, fake * 6, fake, fake, 64, fake,
+                           0, 10, 0.01, 1, ttt.TTT_F32, 6, None, None, fake, 1 << 30, None)
+    assert st == -1 and b"flag" in lib.ttt_last_error()
+    st = lib.ttt_stream_ex(1, 64, 128, fake, fake * 2, fake * 3, fake, fake, 64, fake, 0, fake, 64, fake * 8, 64, 10,
+                           5, 0.01, 1, ttt.TTT_F32, 2, fake, 1 << 30, None)
+    assert st == -1 and b"flag" in lib.ttt_last_error()
+    # gate: channels not a multiple of 64, bad eps, overlap, misaligned W_g
+    st = lib.ttt_output_gate(96, fake, 96, fake * 4, fake * 8, 1e-6, fake * 16, 96, 10, ttt.TTT_BF16, None)
+    assert st == -2
+    st = lib.ttt_output_gate(64, fake, 64, fake * 4, fake * 8, -1.0, fake * 16, 64, 10, ttt.TTT_BF16, None)
+    assert st == -1 and b"eps" in lib.ttt_last_error()
+    st = lib.ttt_output_gate(64, fake, 64, fake * 4, fake * 8, 1e-6, fake + 64, 64, 10, ttt.TTT_BF16, None)
+    assert st == -1 and b"overlap" in lib.ttt_last_error()
+    st = lib.ttt_output_gate(64, fake, 64, fake * 4 + 2, fake * 8, 1e-6, fake * 16, 64, 10, ttt.TTT_BF16, None)
+    assert st == -1 and b"wg" in lib.ttt_last_error()
+    st = lib.ttt_output_gate(64, fake, 32, fake * 4, fake * 8, 1e-6, fake * 16, 64, 10, ttt.TTT_BF16, None)
+    assert st == -1
+    # n = 0 launches nothing and succeeds
+    assert lib.ttt_output_gate(64, None, 64, None, None, 1e-6, None, 64, 0, ttt.TTT_BF16, None) == 0
