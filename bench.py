@@ -76,6 +76,11 @@ def flops(cfg, n, nq):
     return grad, apply, ns, conv
 
 
+def gate_flops(cfg, nq):
+    """Gated output: the C x C gate product per apply row (RMSNorm/SiLU not counted)."""
+    return 2.0 * nq * (cfg.heads * cfg.d) ** 2 if cfg.gate else 0.0
+
+
 def copy_calibration():
     import torch
     n = 1 << 30   # 1 GiB
@@ -106,15 +111,24 @@ def cpu_baseline(cfg, frames):
                     n_special=cfg.n_special, grid_h=cfg.grid_h, grid_w=cfg.grid_w)
     t0 = time.perf_counter()
     if cfg.chunk_frames:
-        oracle.stream(*args, cfg.lr, cfg.steps, chunk=cfg.chunk_frames * cfg.tokens_per_frame)
+        oracle.stream(*args, cfg.lr, cfg.steps, chunk=cfg.chunk_frames * cfg.tokens_per_frame,
+                      norm_preserve=cfg.norm_preserve)
     else:
-        oracle.layer(*args, cfg.lr, cfg.steps, conv=conv)
+        if conv is not None:
+            args[4] = oracle.shortconv2d(args[4], **conv)
+        w_hat, _, _ = oracle.update(*args[:6], cfg.lr, cfg.steps, norm_preserve=cfg.norm_preserve)
+        o = oracle.apply(*w_hat, args[6])
+        if cfg.gate:
+            wg, gamma = synth.gate_weights(cfg.seed, cfg.heads * cfg.d, inp.k.dtype)
+            oracle.output_gate(o, f32(wg), f32(gamma), cfg.gate_eps)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{frames} frames x {cfg.tokens_per_frame} tokens = {n} tokens of {cfg.name}, "
                       f"fp32 NumPy oracle, full layer (conv={cfg.conv}, steps={cfg.steps}, apply"
-                      f"{', streamed in chunks' if cfg.chunk_frames else ''}), "
+                      f"{', streamed in chunks' if cfg.chunk_frames else ''}"
+                      f"{', norm-preserving step' if cfg.norm_preserve else ''}"
+                      f"{', gated output' if cfg.gate else ''}), "
                       f"{dt:.2f} s wall"}
 
 
@@ -210,20 +224,27 @@ def main():
         def step():
             for a, b in zip(w_out, w0):
                 a.copy_(b)
-            ttt.stream(w_out, inp.k, inp.v, inp.eta, inp.q, cfg.lr, cfg.steps, chunk, out=o, workspace=ws)
+            ttt.stream(w_out, inp.k, inp.v, inp.eta, inp.q, cfg.lr, cfg.steps, chunk, out=o, workspace=ws,
+                       norm_preserve=cfg.norm_preserve)
     else:
         v2 = torch.empty_like(inp.v)
         ws_u = torch.empty(ttt.update_workspace_bytes(H, d, m, n, dt), dtype=torch.uint8, device="cuda")
         nws = ttt.apply_workspace_bytes(H, d, m, nq, dt)
         ws_a = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        if cfg.gate:
+            wg, gamma = (t.cuda() for t in synth.gate_weights(cfg.seed, H * d, dt))
+            o_gated = torch.empty_like(o)
 
         def step():
             v = inp.v
             if cfg.conv:
                 ttt.shortconv2d(inp.v, inp.wconv, **geo, out=v2)
                 v = v2
-            ttt.update(w0, inp.k, v, inp.eta, cfg.lr, cfg.steps, out=w_out, workspace=ws_u)
+            ttt.update(w0, inp.k, v, inp.eta, cfg.lr, cfg.steps, out=w_out, workspace=ws_u,
+                       norm_preserve=cfg.norm_preserve)
             ttt.apply(w_out, inp.q, out=o, workspace=ws_a)
+            if cfg.gate:
+                ttt.output_gate(o, wg, gamma, cfg.gate_eps, out=o_gated)
 
     for _ in range(args.warmup):
         step()
@@ -257,7 +278,8 @@ def main():
         "config": {"workload": cfg.name, "frames": cfg.frames, "tokens_per_frame": cfg.tokens_per_frame,
                    "update_tokens": n, "apply_tokens": nq, "heads": H, "d": d, "hidden": m,
                    "inner_steps": cfg.steps, "shortconv2d": cfg.conv, "lr": cfg.lr,
-                   "stream_chunk_tokens": chunk or None},
+                   "stream_chunk_tokens": chunk or None, "norm_preserving_step": cfg.norm_preserve,
+                   "gated_output": cfg.gate},
         "input_gen_s": round(gen_s, 2),
     }
     peak = PEAK_BF16_TFLOPS if dt == torch.bfloat16 else PEAK_F32_TFLOPS
@@ -267,8 +289,9 @@ def main():
         per_kernel = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
                       for k, v in kt.items()}
         out["kernels"] = per_kernel
-        gemm_flops = (grad_f * cfg.steps + apply_f) * args.steps
-        out["mfma_pct_gemm_phases"] = 100.0 * gemm_flops / ((g_ms + a_ms) * 1e-3) / (peak * 1e12)
+        gemm_flops = (grad_f * cfg.steps + apply_f + gate_flops(cfg, nq)) * args.steps
+        gemm_ms = g_ms + a_ms + (kt["gate"][0] if cfg.gate else 0.0)
+        out["mfma_pct_gemm_phases"] = 100.0 * gemm_flops / (gemm_ms * 1e-3) / (peak * 1e12)
         out["mfma_pct_whole_layer"] = (100.0 * (gemm_flops + ns_f * cfg.steps * updates_per_step * args.steps)
                                        / elapsed / (peak * 1e12))
         grad_avg_s = g_ms * 1e-3 / g_n
@@ -284,6 +307,13 @@ def main():
             out["apply_kernel"] = {"achieved_tflops": apply_launch_f / a_avg / 1e12,
                                    "frac": apply_launch_f / a_avg / 1e12 / peak,
                                    "avg_launch_ms": a_avg * 1e3}
+        if cfg.gate and kt["gate"][1]:
+            q_ms, q_n = kt["gate"]
+            q_avg = q_ms * 1e-3 / q_n
+            q_f = gate_flops(cfg, nq)
+            out["gate_kernel"] = {"achieved_tflops": q_f / q_avg / 1e12, "peak": peak,
+                                  "frac": q_f / q_avg / 1e12 / peak, "avg_launch_ms": q_avg * 1e3,
+                                  "flop_per_launch": q_f}
         if cfg.conv and kt["conv"][1]:
             c_avg = kt["conv"][0] * 1e-3 / kt["conv"][1]
             conv_bytes = 2.0 * n * H * d * inp.v.element_size()

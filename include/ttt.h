@@ -175,7 +175,7 @@ int ttt_shortconv2d(const void *v, void *v_out, int64_t ld, const float *wconv,
  * o_in, o_out : [n][ld_in] / [n][ld_out] device rows, `dtype`, columns [0, C)
  *               used; must not overlap each other or wg.
  * wg          : [C][C] row-major, `dtype`, device, 16-byte aligned.
- * gamma       : [C] fp32, device.
+ * gamma       : [C] fp32, device, 16-byte aligned.
  * eps         : >= 0, finite.
  * Requires C >= 64, C % 64 == 0, C <= ld_in, C <= ld_out, and the row
  * alignment of the conventions above.  n = 0 launches nothing.  The products

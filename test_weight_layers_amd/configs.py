@@ -45,6 +45,9 @@ class LayerConfig:
     norm_k: bool = True
     norm_v: bool = False
     chunk_frames: int = 0  # >0: streaming, apply-then-update per chunk
+    norm_preserve: bool = False   # ZipMap's norm-preserving weight step
+    gate: bool = False     # ZipMap's gated output unit on the apply rows
+    gate_eps: float = 1e-6
 
     @property
     def n(self) -> int:
@@ -91,6 +94,11 @@ CONFIGS = {
                        tokens_per_frame=VGGT_TOKENS, grid_h=VGGT_GRID, grid_w=VGGT_GRID,
                        n_special=VGGT_SPECIAL, extra_query=0, steps=1, conv=False, dtype="bf16",
                        seed=5, chunk_frames=32),
+    # ZipMap-750 with ZipMap's stabilisers: norm-preserving step, gated output.
+    "c4z": LayerConfig("c4z-zipmap-750-stabilised", heads=4, d=256, m=512, frames=750,
+                       tokens_per_frame=VGGT_TOKENS, grid_h=VGGT_GRID, grid_w=VGGT_GRID,
+                       n_special=VGGT_SPECIAL, extra_query=64 * VGGT_TOKENS, steps=1, conv=False,
+                       dtype="bf16", seed=3, norm_preserve=True, gate=True),
     # ZipMap's own single-state shape (d=1024, hidden 2048, 6d^2 state).
     "zipmap1h": LayerConfig("zipmap-1head-d1024", heads=1, d=1024, m=2048, frames=750,
                             tokens_per_frame=VGGT_TOKENS, grid_h=VGGT_GRID, grid_w=VGGT_GRID,

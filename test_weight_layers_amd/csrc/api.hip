@@ -500,7 +500,8 @@ int ttt_output_gate(int32_t channels, const void *o_in, int64_t ld_in, const voi
   if ((st = check_rows(o_in, ld_in, 1, channels, dtype, "o_in"))) return st;
   if ((st = check_rows(o_out, ld_out, 1, channels, dtype, "o_out"))) return st;
   if (!wg || reinterpret_cast<uintptr_t>(wg) % 16 != 0) return fail(TTT_EINVAL, "wg is null or not 16-byte aligned");
-  if (!gamma) return fail(TTT_EINVAL, "gamma is null");
+  if (!gamma || reinterpret_cast<uintptr_t>(gamma) % 16 != 0)
+    return fail(TTT_EINVAL, "gamma is null or not 16-byte aligned");
   const size_t es = esize(dtype);
   const size_t in_b = (size_t)n * ld_in * es, out_b = (size_t)n * ld_out * es, wg_b = (size_t)channels * channels * es;
   if (overlap(o_in, in_b, o_out, out_b)) return fail(TTT_EINVAL, "o_in and o_out must not overlap");

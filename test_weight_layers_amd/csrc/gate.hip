@@ -3,14 +3,18 @@
 //
 // One fused kernel: the gate pre-activation O' W_g^T is a dense contraction
 // (n x C x C) on bf16 (or fp32) MFMA; the row sums of squares for the RMS are
-// taken from the same O' pieces as they pass through registers on their way to
-// LDS, and the epilogue multiplies the normalised input by SiLU of the product,
-// so neither the pre-activation nor the norm ever goes to HBM.
+// taken from the O' operand fragments of the product, and the epilogue
+// multiplies the normalised input by SiLU of the product, so neither the
+// pre-activation nor the norm ever goes to HBM.
 //
-// Workgroup: 8 waves, a 256-token x 128-channel output tile; wave w owns tokens
-// 64 (w % 4) .. +64 and channels 64 (w / 4) .. +64 (4 x 4 MFMA 16x16 tiles).
-// The reduction runs over C in chunks of 128 bytes per row (64 bf16 / 32 fp32),
-// double-buffered in LDS with the next chunk's global loads in flight.
+// Workgroup: 8 waves, a 256-token x 256-channel output tile; wave w owns tokens
+// 64 (w % 4) .. +64 and channels 128 (w / 4) .. +128 (4 x 8 MFMA 16x16 tiles),
+// so every staged byte feeds 128 multiply-adds: the L2 -> LDS supply of about
+// 12-18 bytes per clock per CU, not the MFMA rate, is what a narrower tile hits.
+// The reduction runs over C in chunks of 32 elements (one MFMA step), DMA'd from
+// global memory straight into a ring of LDS stages (4 x 32 KB for bf16, 2 x 64 KB
+// for fp32), NST - 1 chunks ahead of the one being multiplied.  The RMS sums of
+// squares come from the O' fragments the channel-0 waves already hold.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,48 +22,81 @@ namespace ttt {
 namespace {
 
 constexpr int kGateTok = 256;     // tokens per workgroup
-constexpr int kGateCh = 128;      // output channels per workgroup
-constexpr int kRowB = 128;        // bytes of one row of a staged chunk
+constexpr int kGateCh = 256;      // output channels per workgroup
 
-struct GateSmem {
-  unsigned char a[2][kGateTok * kRowB];
-  unsigned char b[2][kGateCh * kRowB];
-  float rinv[kGateTok];
+template <typename T> struct GateGeo {
+  static constexpr int kRowB = 32 * (int)sizeof(T);     // one chunk of a row: 64 / 128 bytes
+  static constexpr int kPieces = kRowB / 16;            // 16-byte pieces per row
+  static constexpr int kRowsPerKb = 1024 / kRowB;       // rows per 1 KB DMA piece
+  static constexpr int kStageA = kGateTok * kRowB;
+  static constexpr int kStage = kStageA + kGateCh * kRowB;
+  static constexpr int kNst = sizeof(T) == 2 ? 4 : 2;   // ring depth
+  static constexpr int kDmaA = kStageA / 1024 / 8;      // 1 KB DMAs per wave per stage (A part)
+  static constexpr int kDmaB = kGateCh * kRowB / 1024 / 8;
+  static constexpr int kDma = kDmaA + kDmaB;
 };
 
-// 16-byte piece c (0..7) of staged row r.  Fragment reads take 16 rows at one
-// piece (16 lanes per LDS cycle for 16-byte reads): rows r and r + 2q land on
-// the same banks without a swizzle, so the piece index is XORed with r / 2.
-__device__ __forceinline__ int gate_slot(int r, int c) { return r * kRowB + ((c ^ ((r >> 1) & 7)) << 4); }
-
-template <typename T> __device__ __forceinline__ typename FragOf<T>::type gate_frag(const unsigned char *s, int r,
-                                                                                   int piece);
-template <> __device__ __forceinline__ bf16x8 gate_frag<__bf16>(const unsigned char *s, int r, int piece) {
-  return *reinterpret_cast<const bf16x8 *>(s + gate_slot(r, piece));
+// Piece c of staged row r sits at position c ^ swizzle(r).  Fragment reads take
+// 16 consecutive rows at one piece (16 lanes per LDS cycle for 16-byte reads).
+// 64-byte rows (4 per 256-byte bank line): swz_64 spreads rows R..R+15 over 16
+// positions.  128-byte rows: rows r and r + 2q collide without a swizzle, so the
+// piece index is XORed with r / 2.
+template <typename T> __device__ __forceinline__ int gate_swz(int r);
+template <> __device__ __forceinline__ int gate_swz<__bf16>(int r) { return swz_64(r); }
+template <> __device__ __forceinline__ int gate_swz<float>(int r) { return (r >> 1) & 7; }
+template <typename T> __device__ __forceinline__ int gate_slot(int r, int c) {
+  return r * GateGeo<T>::kRowB + ((c ^ gate_swz<T>(r)) << 4);
 }
-template <> __device__ __forceinline__ f32x8 gate_frag<float>(const unsigned char *s, int r, int piece) {
-  const f32x4 lo = *reinterpret_cast<const f32x4 *>(s + gate_slot(r, piece));
-  const f32x4 hi = *reinterpret_cast<const f32x4 *>(s + gate_slot(r, piece + 1));
+
+// lane group g's 8 reduction elements 8g .. 8g+7 of staged row r
+template <typename T> __device__ __forceinline__ typename FragOf<T>::type gate_frag(const unsigned char *s, int r,
+                                                                                   int g);
+template <> __device__ __forceinline__ bf16x8 gate_frag<__bf16>(const unsigned char *s, int r, int g) {
+  return *reinterpret_cast<const bf16x8 *>(s + gate_slot<__bf16>(r, g));
+}
+template <> __device__ __forceinline__ f32x8 gate_frag<float>(const unsigned char *s, int r, int g) {
+  const f32x4 lo = *reinterpret_cast<const f32x4 *>(s + gate_slot<float>(r, 2 * g));
+  const f32x4 hi = *reinterpret_cast<const f32x4 *>(s + gate_slot<float>(r, 2 * g + 1));
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ float piece_sumsq(u32x4 raw, __bf16) {
-  const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
+__device__ __forceinline__ float frag_sumsq(const bf16x8 v) {
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) s += (float)v[i] * (float)v[i];
   return s;
 }
-__device__ __forceinline__ float piece_sumsq(u32x4 raw, float) {
-  const f32x4 v = __builtin_bit_cast(f32x4, raw);
-  return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+__device__ __forceinline__ float frag_sumsq(const f32x8 v) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += v[i] * v[i];
+  return s;
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Workgroup barrier without the vmcnt(0) that __syncthreads adds (which would
+// also wait for the DMAs just issued for later stages).
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <typename T>
 __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
-  __shared__ __attribute__((aligned(16))) GateSmem sm;
-  constexpr int E = 16 / (int)sizeof(T);          // elements per 16-byte piece
-  constexpr int KS = E / 4;                       // 32-element MFMA steps per 128-byte chunk
+  using G = GateGeo<T>;
+  constexpr int NST = G::kNst;
+  // the ring's stages are separate arrays so that the compiler can tell the
+  // stage being read from the ones the DMAs are filling
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[G::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[G::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[NST > 2 ? G::kStage : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[NST > 3 ? G::kStage : 16];
+  __shared__ float rinv[kGateTok];
   const int t = threadIdx.x;
   const int C = p.channels;
   const int tiles_c = (C + kGateCh - 1) / kGateCh;
@@ -73,105 +110,171 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
   const int j0 = (int)(item % tiles_c) * kGateCh;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 4, li = l & 15;
   const int wr = w & 3, wc = w >> 2;
-  const bool active = j0 + 64 * wc < C;           // wave-uniform: this wave's channels exist
+  const bool active = j0 + 128 * wc < C;          // wave-uniform: this wave's channels exist
 
   const T *oin = static_cast<const T *>(p.o_in);
   const T *wg = static_cast<const T *>(p.wg);
-  const int pc = t & 7;                           // piece column of this thread's loads
-  const int lrow = t >> 3;                        // rows lrow + 64 u
-  const T *asrc[4];
-  const T *bsrc[2];
+  // DMA sources.  1 KB piece b of a stage's A part holds rows kRowsPerKb * b ..
+  // (wave w fills b = kDmaA w ..), of its B part likewise; lane l writes row
+  // kRowsPerKb b + l / kPieces at position l % kPieces, which holds the row's
+  // piece (l % kPieces) ^ swizzle.
+  const char *asrc[G::kDmaA];
+  const char *bsrc[G::kDmaB];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    int64_t tok = tok0 + lrow + 64 * u;
+  for (int j = 0; j < G::kDmaA; ++j) {
+    const int r = G::kRowsPerKb * (G::kDmaA * w + j) + l / G::kPieces;
+    int64_t tok = tok0 + r;
     if (tok >= p.n) tok = p.n - 1;
-    asrc[u] = oin + tok * p.ld_in + pc * E;
+    asrc[j] = reinterpret_cast<const char *>(oin + tok * p.ld_in) + 16 * ((l % G::kPieces) ^ gate_swz<T>(r));
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    int ch = j0 + lrow + 64 * u;
+  for (int j = 0; j < G::kDmaB; ++j) {
+    const int r = G::kRowsPerKb * (G::kDmaB * w + j) + l / G::kPieces;
+    int ch = j0 + r;
     if (ch >= C) ch = C - 1;
-    bsrc[u] = wg + (int64_t)ch * C + pc * E;
+    bsrc[j] = reinterpret_cast<const char *>(wg + (int64_t)ch * C) + 16 * ((l % G::kPieces) ^ gate_swz<T>(r));
   }
-  u32x4 ra[4], rb[2];
+  auto issue = [&](int kc, unsigned char *dst) __attribute__((always_inline)) {
+    const int64_t kb = (int64_t)kc * G::kRowB;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) ra[u] = *reinterpret_cast<const u32x4 *>(asrc[u]);
+    for (int j = 0; j < G::kDmaA; ++j) copy16_to_lds(asrc[j] + kb, dst + (G::kDmaA * w + j) * 1024);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) rb[u] = *reinterpret_cast<const u32x4 *>(bsrc[u]);
+    for (int j = 0; j < G::kDmaB; ++j) copy16_to_lds(bsrc[j] + kb, dst + G::kStageA + (G::kDmaB * w + j) * 1024);
+  };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][8];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[a][e] = f32x4{0, 0, 0, 0};
+    for (int e = 0; e < 8; ++e) acc[a][e] = f32x4{0, 0, 0, 0};
   float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = C / (8 * E);
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
+  auto compute = [&](const unsigned char *stage) __attribute__((always_inline)) {
+    if (!active) return;
+    typename FragOf<T>::type fa[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<u32x4 *>(sm.a[buf] + gate_slot(lrow + 64 * u, pc)) = ra[u];
-      ss[u] += piece_sumsq(ra[u], T{});
+    for (int a = 0; a < 4; ++a) fa[a] = gate_frag<T>(stage, 64 * wr + 16 * a + li, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const typename FragOf<T>::type fb = gate_frag<T>(stage + G::kStageA, 128 * wc + 16 * e + li, g);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[a][e] = mma(fa[a], fb, acc[a][e]);
     }
+    if (wc == 0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4 *>(sm.b[buf] + gate_slot(lrow + 64 * u, pc)) = rb[u];
-    __syncthreads();
-    if (kc + 1 < nk) {
-      const int64_t k1 = (int64_t)(kc + 1) * 8 * E;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ra[u] = *reinterpret_cast<const u32x4 *>(asrc[u] + k1);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) rb[u] = *reinterpret_cast<const u32x4 *>(bsrc[u] + k1);
+      for (int a = 0; a < 4; ++a) ss[a] += frag_sumsq(fa[a]);
     }
-    if (active) {
+  };
+  const int nk = C / 32;
+  // one chunk: wait for its stage (the later chunks' DMAs may stay in flight),
+  // barrier, refill the stage read one chunk ago with chunk kc + NST - 1, multiply
+  auto step = [&](int kc, const unsigned char *cur, unsigned char *refill) __attribute__((always_inline)) {
+    const int later = nk - 1 - kc;                // chunks after kc already issued: min(later, NST - 2)
+    if (NST > 3 && later >= 2)
+      wait_vmcnt<2 * G::kDma>();
+    else if (NST > 2 && later >= 1)
+      wait_vmcnt<G::kDma>();
+    else
+      wait_vmcnt<0>();
+    bare_barrier();
+    if (kc + NST - 1 < nk) issue(kc + NST - 1, refill);
+    compute(cur);
+  };
+  unsigned char *const ring[4] = {st0, st1, st2, st3};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        // lane group g takes elements 32 ks + 8 g .. +8 of the chunk
-        const int piece = (32 * ks + 8 * g) * (int)sizeof(T) / 16;
-        typename FragOf<T>::type fa[4], fb[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) fa[a] = gate_frag<T>(sm.a[buf], 64 * wr + 16 * a + li, piece);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fb[e] = gate_frag<T>(sm.b[buf], 64 * wc + 16 * e + li, piece);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[a][e] = mma(fa[a], fb[e], acc[a][e]);
-      }
-    }
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) issue(s, ring[s]);
+  for (int kc = 0; kc < nk; kc += NST) {
+    step(kc, st0, ring[NST - 1]);
+    if (kc + 1 < nk) step(kc + 1, st1, st0);
+    if (NST > 2 && kc + 2 < nk) step(kc + 2, st2, st1);
+    if (NST > 3 && kc + 3 < nk) step(kc + 3, st3, st2);
   }
 
-  // row sums of squares: the 8 threads of a row are 8 consecutive lanes
-  const float invc = 1.0f / (float)C;
+  // row sums of squares: lanes li, li+16, li+32, li+48 of a channel-0 wave hold
+  // the four element groups of row 64 wr + 16 a + li
+  if (wc == 0) {
+    const float invc = 1.0f / (float)C;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float s = ss[u];
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (pc == 0) sm.rinv[lrow + 64 * u] = 1.0f / sqrtf(s * invc + p.eps);
+    for (int a = 0; a < 4; ++a) {
+      float s = ss[a];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (g == 0) rinv[64 * wr + 16 * a + li] = 1.0f / sqrtf(s * invc + p.eps);
+    }
   }
-  __syncthreads();
-  if (!active) return;
-
   T *out = static_cast<T *>(p.o_out);
+  if constexpr (sizeof(T) == 2) {
+    // bf16: SiLU(z) goes through LDS (the ring is free now) as a 256 x 256 bf16
+    // tile, rows 64 b .. 64 b + 63 in stage b; then every thread finishes 8
+    // consecutive channels of a row with 16-byte loads of O' and 16-byte stores.
+    // Tile column c of row r sits at c ^ (16 ((r / 4) % 4)), so the four row
+    // groups of a 2-byte store wave land on distinct banks.
+    auto zrow = [&](int blk) __attribute__((always_inline)) -> __bf16 * {
+      return reinterpret_cast<__bf16 *>(blk == 0 ? st0 : blk == 1 ? st1 : blk == 2 ? st2 : st3);
+    };
+    __syncthreads();                  // every wave is done with the ring
+    if (active) {
+      __bf16 *zt = zrow(wr);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int ch = j0 + 64 * wc + 16 * e + li;
-    if (ch >= C) continue;
-    const float gam = p.gamma[ch];
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+        for (int z = 0; z < 4; ++z) {
+          const int r = 16 * a + 4 * g + z;                        // row inside the block
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const int row = 64 * wr + 16 * a + 4 * g + z;
-        const int64_t tok = tok0 + row;
-        if (tok >= p.n) continue;
-        const float x = to_f32(oin[tok * p.ld_in + ch]);
-        const float zg = acc[a][e][z];
-        out[tok * p.ld_out + ch] = from_f32<T>(gam * x * sm.rinv[row] * (zg * sigmoid_fast(zg)));
-      }
+          for (int e = 0; e < 8; ++e) {
+            const float zg = acc[a][e][z];
+            const int c = (128 * wc + 16 * e + li) ^ (16 * g);     // (r / 4) % 4 == g
+            zt[r * kGateCh + c] = (__bf16)(zg * sigmoid_fast(zg));
+          }
+        }
+    }
+    __syncthreads();
+    const int cv = t & 31;                      // 8-channel group of the tile
+    const int ch = j0 + 8 * cv;
+    if (ch >= C) return;
+    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(p.gamma + ch);
+    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(p.gamma + ch + 4);
+    // all 16 rows' O' loads in flight at once (rows past n read row n - 1)
+    bf16x8 xs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int64_t tok = tok0 + 16 * i + (t >> 5);
+      if (tok >= p.n) tok = p.n - 1;
+      xs[i] = *reinterpret_cast<const bf16x8 *>(oin + tok * p.ld_in + ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 16 * i + (t >> 5);
+      const int64_t tok = tok0 + row;
+      const int r = row & 63;
+      const bf16x8 sz = *reinterpret_cast<const bf16x8 *>(zrow(i >> 2) + r * kGateCh + ((8 * cv) ^ (16 * ((r >> 2) & 3))));
+      const float ri = rinv[row];
+      bf16x8 y;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[u] = (__bf16)((u < 4 ? g0[u] : g1[u - 4]) * (float)xs[i][u] * ri * (float)sz[u]);
+      if (tok < p.n) *reinterpret_cast<bf16x8 *>(out + tok * p.ld_out + ch) = y;
+    }
+  } else {
+    __syncthreads();
+    if (!active) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ch = j0 + 128 * wc + 16 * e + li;
+      if (ch >= C) continue;
+      const float gam = p.gamma[ch];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          const int row = 64 * wr + 16 * a + 4 * g + z;
+          const int64_t tok = tok0 + row;
+          if (tok >= p.n) continue;
+          const float x = to_f32(oin[tok * p.ld_in + ch]);
+          const float zg = acc[a][e][z];
+          out[tok * p.ld_out + ch] = from_f32<T>(gam * x * rinv[row] * (zg * sigmoid_fast(zg)));
+        }
+    }
   }
 }
 
