@@ -43,24 +43,36 @@ def parse():
     return ap.parse_args()
 
 
+def grad_source_digest():
+    """sha256 over what the gradient kernel is compiled from: grad.hip, common.h and
+    the part of kernels.h up to the end of GradParams (tile constants and the
+    parameter block); declarations after it belong to other kernels."""
+    import hashlib
+    csrc = os.path.join(ROOT, "test_weight_layers_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("grad.hip", "common.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(csrc, "kernels.h"), "rb") as fh:
+        text = fh.read()
+    start = text.index(b"struct GradParams")
+    h.update(text[:text.index(b"};", start) + 2])
+    return h.hexdigest()
+
+
 def measured_traffic(d):
     """HBM bytes per launch of the gradient kernel from the committed rocprofv3 counter summary,
     or None when the kernel's source changed since the counters were taken (or d differs)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "lact_c5a_hbm_traffic.md")
     if d != 256 or not os.path.exists(path):
         return None
-    h = hashlib.sha256()
-    for f in ("grad.hip", "common.h", "kernels.h"):
-        with open(os.path.join(ROOT, "test_weight_layers_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
     rec = {}
     for line in open(path):
         if line.startswith("traffic_bytes_per_launch grad_fast_kernel<256>:"):
             rec["bytes"] = float(line.split(":")[1])
-        elif line.startswith("source_sha256 grad.hip+common.h+kernels.h:"):
+        elif line.startswith("gradient_kernel_source_sha256:"):
             rec["sha"] = line.split(":")[1].strip()
-    if rec.get("sha") != h.hexdigest():
+    if rec.get("sha") != grad_source_digest():
         return None
     return rec.get("bytes")
 
