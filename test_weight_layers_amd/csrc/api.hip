@@ -117,11 +117,11 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ----------------------------------------------------------------- update plan
 struct UpdatePlan {
   int H, d, m, r, c;
-  bool bf16, fast, xcd;
+  bool bf16, fast, xcd, big;
   int dchunks, splits, grid;
-  int64_t n, nblk;
+  int64_t n, nblk, n_pad;
   size_t off_wop, off_part, off_g, off_sumsq, off_x0, off_x1, off_xt0, off_xt1, off_a, off_b, off_sync, off_wsq;
-  size_t total;
+  size_t off_inter, total;
 };
 
 UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
@@ -131,7 +131,8 @@ UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
   p.c = d < m ? m : d;
   p.bf16 = dtype == TTT_BF16;
   p.fast = !g_force_general && grad_fast_supported(d, p.bf16);
-  p.dchunks = p.fast ? 1 : d / grad_general_dc(d, p.bf16);
+  p.big = !g_force_general && !p.fast && big_supported(d, m, p.bf16);
+  p.dchunks = p.fast || p.big ? 1 : d / grad_general_dc(d, p.bf16);
   p.nblk = (n + kTokBlock - 1) / kTokBlock;
   const int mtiles = m / kHidTile;
   const int64_t per_split = (int64_t)H * mtiles * p.dchunks;
@@ -142,6 +143,18 @@ UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
   if (s < 1) s = 1;
   p.splits = (int)s;
   p.grid = (int)(per_split * s);
+  if (p.big) {
+    // wide heads: the contraction kernels split the tokens; about 512 workgroups
+    // for the smaller of the two contraction launches
+    p.n_pad = big_pad_tokens(n);
+    const int64_t tiles = (int64_t)H * big_contract_tiles(d, m, 1);
+    int64_t sb = (512 + tiles - 1) / tiles;
+    if (g_splits > 0) sb = g_splits;
+    const int64_t blocks = p.n_pad / 32;
+    if (blocks > 0 && sb > blocks) sb = blocks;
+    p.splits = (int)(sb < 1 ? 1 : sb);
+    p.grid = 0;
+  }
   p.xcd = p.fast && p.grid % 8 == 0 && (p.grid / 8) % mtiles == 0;
   const size_t mat = (size_t)H * d * m;
   size_t off = 0;
@@ -169,12 +182,23 @@ UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
   off = align256(off + (size_t)H * p.splits * 4);
   p.off_wsq = off;                                   // norm-preserving step: 2 x [3H][d*m/4096]
   off = align256(off + 2 * (3 * mat / 4096) * 4);
+  p.off_inter = off;                                 // wide heads: dZ1 | dZ3 | H', [H][n_pad][m] bf16
+  if (p.big) off = align256(off + 3 * (size_t)H * p.n_pad * m * 2);
   p.total = off;
   return p;
 }
 
-size_t apply_ws(int H, int d, int m, int dtype) {
-  return dtype == TTT_BF16 ? align256((size_t)3 * H * d * m * 2) : 0;
+bool apply_big(int d, int m, int dtype) {
+  return dtype == TTT_BF16 && !g_force_general && !apply_fast_supported(d, true) && big_supported(d, m, true);
+}
+
+// bf16: the operand copies (3 H d m); wide heads also the hidden activations
+// H [H][nq_pad][m] of the two-kernel apply
+size_t apply_ws(int H, int d, int m, int64_t nq, int dtype) {
+  if (dtype != TTT_BF16) return 0;
+  size_t b = align256((size_t)3 * H * d * m * 2);
+  if (apply_big(d, m, dtype)) b += align256((size_t)H * big_pad_tokens(nq) * m * 2);
+  return b;
 }
 
 struct W3 {
@@ -239,6 +263,22 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
     gp.heads = P.H, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
     // the hidden tiles of a token range keep pace through these counters (see the kernel)
     if (P.fast && P.xcd) gp.group_sync = reinterpret_cast<unsigned *>(ws + P.off_sync);
+    if (P.big) {
+      BigFwdParams fp{};
+      fp.k = k, fp.v = v, fp.ld = ld, fp.eta = eta, fp.eta_hs = eta_hs;
+      fp.w1 = gp.w1, fp.w3 = gp.w3, fp.w2t = gp.w2t, fp.out = ws + P.off_inter;
+      fp.n = P.n, fp.n_pad = P.n_pad, fp.heads = P.H, fp.d = P.d, fp.m = P.m;
+      BigCtrParams cp{};
+      cp.k = k, cp.v = v, cp.ld = ld, cp.inter = ws + P.off_inter, cp.part = part;
+      cp.n = P.n, cp.n_pad = P.n_pad, cp.heads = P.H, cp.d = P.d, cp.m = P.m, cp.splits = P.splits;
+      st = run(TTT_K_GRAD, "gradient", s, [&] {
+        if (P.n == 0) return launch_zero_u32(reinterpret_cast<unsigned *>(part),
+                                             (int)(3 * mat * (size_t)P.splits), s);
+        const hipError_t e = launch_big_fwd(fp, s);
+        return e != hipSuccess ? e : launch_big_contract(cp, s);
+      });
+      if (st) return st;
+    } else {
     st = run(TTT_K_GRAD, "gradient", s, [&] {
       if (gp.group_sync) {
         const hipError_t e = launch_zero_u32(gp.group_sync, P.H * P.splits, s);
@@ -247,6 +287,7 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
       return launch_grad(gp, P.d, P.bf16, P.fast, P.grid, s);
     });
     if (st) return st;
+    }
     if (fused) {
       NsStepParams np{};
       np.part = part, np.splits = P.splits, np.per_split = (int64_t)3 * mat;
@@ -337,6 +378,19 @@ int do_apply(int H, int d, int m, W3 w, const void *q, int64_t ldq, void *o, int
   if (nq == 0) return TTT_OK;
   const bool bf16 = dtype == TTT_BF16;
   const bool fast = !g_force_general && apply_fast_supported(d, bf16);
+  if (apply_big(d, m, dtype)) {
+    const size_t mat = (size_t)H * d * m;
+    __bf16 *b = reinterpret_cast<__bf16 *>(ws);
+    const int st = run(TTT_K_CAST, "cast", s, [&] {
+      return launch_cast(w.w1, w.w3, w.w2, b, b + mat, nullptr, b + 2 * mat, H, d, m, true, s);
+    });
+    if (st) return st;
+    BigApplyParams bp{};
+    bp.q = q, bp.ldq = ldq, bp.o = o, bp.ldo = ldo, bp.w1 = b, bp.w3 = b + mat, bp.w2 = b + 2 * mat;
+    bp.hbuf = ws + align256(3 * mat * 2);
+    bp.nq = nq, bp.nq_pad = big_pad_tokens(nq), bp.heads = H, bp.d = d, bp.m = m;
+    return run(TTT_K_APPLY, "apply", s, [&] { return launch_big_apply(bp, s); });
+  }
   ApplyParams ap{};
   ap.q = q, ap.ldq = ldq, ap.o = o, ap.ldo = ldo, ap.nq = nq, ap.heads = H, ap.m = m;
   ap.dchunks = fast ? 1 : d / apply_general_dc(d, bf16);
@@ -391,7 +445,7 @@ int ttt_apply_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t nq, i
   if (st) return st;
   if (nq < 0) return fail(TTT_EINVAL, "nq must be >= 0");
   if (!bytes) return fail(TTT_EINVAL, "bytes is null");
-  *bytes = apply_ws(heads, d, m, dtype);
+  *bytes = apply_ws(heads, d, m, nq, dtype);
   return TTT_OK;
 }
 
@@ -400,7 +454,7 @@ int ttt_stream_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t chun
   if (st) return st;
   if (chunk < 1) return fail(TTT_EINVAL, "chunk must be >= 1");
   if (!bytes) return fail(TTT_EINVAL, "bytes is null");
-  const size_t a = plan_update(heads, d, m, chunk, dtype).total, b = apply_ws(heads, d, m, dtype);
+  const size_t a = plan_update(heads, d, m, chunk, dtype).total, b = apply_ws(heads, d, m, chunk, dtype);
   *bytes = a > b ? a : b;
   return TTT_OK;
 }
@@ -460,7 +514,7 @@ int ttt_apply(int32_t heads, int32_t d, int32_t m, const float *w1, const float 
     if (overlap(q, (size_t)nq * ld_q * esize(dtype), o, (size_t)nq * ld_o * esize(dtype)))
       return fail(TTT_EINVAL, "q and o must not overlap");
   }
-  if ((st = check_ws(workspace, workspace_bytes, apply_ws(heads, d, m, dtype)))) return st;
+  if ((st = check_ws(workspace, workspace_bytes, apply_ws(heads, d, m, nq, dtype)))) return st;
   return do_apply(heads, d, m, W3{w1, w3, w2}, q, ld_q, o, ld_o, nq, dtype, static_cast<char *>(workspace),
                   static_cast<hipStream_t>(stream));
 }

@@ -132,6 +132,44 @@ struct GateParams {
 int64_t gate_tiles(int64_t n);
 hipError_t launch_gate(const GateParams &p, bool bf16, hipStream_t s);
 
+// Wide heads (bf16, d in {512, 768, 1024}, m % 256 == 0): the update and apply
+// split at the hidden layer into dense contractions (bigd.hip).
+bool big_supported(int d, int m, bool bf16);
+int64_t big_pad_tokens(int64_t n);          // token rows of the intermediates (multiple of 256)
+int big_contract_tiles(int d, int m, int mode);
+struct BigFwdParams {                       // dZ1, dZ3, H' = SwiGLU backward of K, V against W
+  const void *k, *v;                        // [n][ld] bf16 token rows
+  int64_t ld;
+  const float *eta;
+  int64_t eta_hs;
+  const void *w1, *w3, *w2t;                // [H][m][d] bf16
+  void *out;                                // 3 x [H][n_pad][m] bf16: dZ1 | dZ3 | H'
+  int64_t n, n_pad;
+  int heads, d, m;
+};
+hipError_t launch_big_fwd(const BigFwdParams &p, hipStream_t s);
+struct BigCtrParams {                       // split partials of G1 = dZ1^T K, G3 = dZ3^T K, G2 = V^T H'
+  const void *k, *v;
+  int64_t ld;
+  const void *inter;                        // the forward's output
+  float *part;                              // [splits][3][H][m d]
+  int64_t n, n_pad;
+  int heads, d, m, splits;
+};
+hipError_t launch_big_contract(const BigCtrParams &p, hipStream_t s);
+struct BigApplyParams {                     // H = SiLU(Q W1^T) o (Q W3^T); O = H W2^T
+  const void *q;
+  int64_t ldq;
+  void *o;
+  int64_t ldo;
+  const void *w1, *w3;                      // [H][m][d] bf16
+  const void *w2;                           // [H][d][m] bf16
+  void *hbuf;                               // [H][nq_pad][m] bf16
+  int64_t nq, nq_pad;
+  int heads, d, m;
+};
+hipError_t launch_big_apply(const BigApplyParams &p, hipStream_t s);
+
 hipError_t launch_conv(const void *v, void *out, int64_t ld, const float *w, int frames, int tpf,
                        int nsp, int gh, int gw, int channels, bool bf16, hipStream_t s);
 

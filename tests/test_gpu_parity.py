@@ -86,6 +86,15 @@ def test_zipmap_single_head_1024_2048():
     _check(CONFIGS["zipmap1h"], n=1500, nq_extra=77)
 
 
+@pytest.mark.parametrize("general", [False, True])
+@pytest.mark.parametrize("shape", [(2, 512, 512, 1000, 77), (2, 768, 256, 333, 5), (1, 1024, 512, 70, 300)])
+def test_wide_heads(shape, general):
+    # the two-kernel wide-head path (d >= 512) and the general kernels, both against
+    # the oracle: ragged token tails, fewer tokens than one 256-row tile, Nq > N
+    H, d, m, n, extra = shape
+    _check(cfg_like("c4", heads=H, d=d, m=m), n=n, nq_extra=extra, general=general)
+
+
 def test_two_inner_steps_with_conv():
     cfg = cfg_like("c3", frames=2)
     _check(cfg, steps=2)
