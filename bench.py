@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     ap.add_argument("--no-profile-events", action="store_true")
+    ap.add_argument("--host-stream", type=int, default=0, metavar="BATCH",
+                    help="time the out-of-core update instead: K, V, eta in pinned host memory, streamed "
+                         "in batches of BATCH tokens (PCIe-inclusive; not the headline)")
     ap.add_argument("--sweep", action="store_true",
                     help="time ZipMap-shaped layers at 125..2000 frames and fit t = t0 + beta*N")
     return ap.parse_args()
@@ -196,6 +199,45 @@ def linear_sweep(steps, warmup):
     print(json.dumps(out), flush=True)
 
 
+def host_stream(cfg, batch, steps, warmup):
+    """Out-of-core update of the workload's tokens from pinned host memory (VGG-T3 关键发现 2)."""
+    import torch
+    from test_weight_layers_amd import synth, ttt
+    torch.cuda.set_device(0)
+    ttt.load()
+    inp = synth.make_inputs(cfg, nq_extra=0)
+    H, d, m = cfg.heads, cfg.d, cfg.m
+    n = inp.k.shape[0]
+    kh, vh, eh = inp.k.pin_memory(), inp.v.pin_memory(), inp.eta.contiguous().pin_memory()
+    w0 = tuple(t.cuda() for t in (inp.w1, inp.w3, inp.w2))
+    w_out = tuple(torch.empty_like(x) for x in w0)
+    ws = torch.empty(ttt.update_host_workspace_bytes(H, d, m, batch, kh.stride(0), kh.dtype), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        ttt.update_host(w0, kh, vh, eh, cfg.lr, cfg.steps, batch=batch, out=w_out, workspace=ws,
+                        norm_preserve=cfg.norm_preserve)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ttt.profile_reset()
+    ttt.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ttt.profile_enable(False)
+    kt = ttt.profile_read()
+    bytes_h2d = 2.0 * n * kh.stride(0) * kh.element_size() * cfg.steps + 4.0 * H * n * cfg.steps
+    print(json.dumps({"mode": "out-of-core update (host-streamed K, V, eta)", "workload": cfg.name,
+                      "update_tokens": n, "inner_steps": cfg.steps, "batch_tokens": batch,
+                      "tokens_per_s": n * steps / el, "ms_per_update": el * 1e3 / steps,
+                      "h2d_gb_per_update": bytes_h2d / 1e9, "h2d_gbs": bytes_h2d * steps / el / 1e9,
+                      "gradient_kernel_ms_per_update": kt["grad"][0] / steps}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,6 +257,9 @@ def main():
     cfg = CONFIGS[args.config]
     if args.frames:
         cfg = cfg.with_frames(args.frames)
+    if args.host_stream:
+        host_stream(cfg, args.host_stream, args.steps, args.warmup)
+        return
     torch.cuda.set_device(0)
     ttt.load()
     t_gen = time.perf_counter()

@@ -132,6 +132,42 @@ int ttt_update_ex(int32_t heads, int32_t d, int32_t m,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ttt_update_host -- ttt_update_ex with K, V and eta in HOST memory, streamed to
+ * the GPU in batches of `batch` tokens ([VGG-T3] 关键发现 2 and 亮点 2: the TTT
+ * objective is a sum over tokens, so the gradient of any token set is the sum of
+ * its minibatches' gradients, and sets larger than device memory can be
+ * processed with the minibatches offloaded to the CPU).
+ *
+ * For each inner step, every batch is copied host -> device into one of two
+ * staging slots of the workspace (on a copy stream the library creates once per
+ * device, default priority) while the previous batch's gradient runs on `stream`;
+ * each batch's gradient is added to a running fp32 G in a fixed order, and the
+ * optimiser step (Newton-Schulz, W update, TTT_NORM_PRESERVE) then runs on G as in
+ * ttt_update_ex.  steps = 2 streams the tokens twice.  The result equals
+ * ttt_update_ex on the same tokens up to the fp32 order of the sum over tokens;
+ * it is deterministic for a given batch.
+ *
+ * k, v      : HOST rows [n][ld_kv] (`dtype`); (ld_kv * element size) % 16 == 0.
+ *             Page-locked memory (hipHostMalloc) lets the copies overlap the
+ *             kernels; pageable memory works but copies synchronously.
+ * eta       : HOST rates, eta[h * eta_head_stride + i] (stride 0: shared).
+ * w*, w*_out: DEVICE fast weights as in ttt_update_ex.
+ * batch     : tokens per staged batch (>= 1; the limits of ttt_update apply to it).
+ * workspace : DEVICE, >= ttt_update_host_workspace_bytes(H, d, m, batch, ld_kv, dtype).
+ * Host buffers must stay unchanged until the work on `stream` has completed.
+ */
+int ttt_update_host_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t batch, int64_t ld_kv,
+                                    int32_t dtype, size_t *bytes);
+int ttt_update_host(int32_t heads, int32_t d, int32_t m,
+                    const float *w1, const float *w3, const float *w2,
+                    float *w1_out, float *w3_out, float *w2_out,
+                    const void *k, const void *v, int64_t ld_kv,
+                    const float *eta, int64_t eta_head_stride,
+                    int64_t n, int64_t batch, float lr, int32_t steps, int32_t dtype, uint32_t flags,
+                    float *grad_out, float *ns_out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ttt_apply -- o_i = f_W(q_i) for every row ([Scal3R] eq. (4); [ZipMap]
  * 关键设计 1; [tttLRM] query-only tokens use the same call).
  *

@@ -213,17 +213,81 @@ constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
 constexpr int kNsIters = 5;
 constexpr float kNsEps = 1e-7f;
 
-// ops_ready: the operand copies of `in` are already at the start of the workspace
-// (written by the previous call's last step or by an apply cast of the same layout).
-// keep_ops: the last step leaves the operand copies of `out` there.
-// norm: the norm-preserving step (W^ = ||W|| (W - lr NS) / ||W - lr NS|| per matrix).
-int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v, int64_t ld, const float *eta,
-              int64_t eta_hs, float lr, int steps, float *grad_out, float *ns_out, char *ws, hipStream_t s,
-              bool norm, bool ops_ready = false, bool keep_ops = false) {
-  const bool fused = !g_ns_unfused;
+// Operand copies of `src` at the start of the workspace (bf16 W1, W3, W2^T; fp32
+// mode only W2^T), cast unless `ready`.  Returns the pointers the gradient reads.
+struct GradOps {
+  const void *w1, *w3, *w2t;
+};
+int prepare_operands(const UpdatePlan &P, W3 src, bool ready, char *ws, hipStream_t s, GradOps *ops) {
   const size_t mat = (size_t)P.H * P.d * P.m;
   void *const wop = ws + P.off_wop;
-  float *part = reinterpret_cast<float *>(ws + P.off_part);
+  if (P.bf16) {
+    __bf16 *b = static_cast<__bf16 *>(wop);
+    if (!ready) {
+      const int st = run(TTT_K_CAST, "cast", s, [&] {
+        return launch_cast(src.w1, src.w3, src.w2, b, b + mat, b + 2 * mat, nullptr, P.H, P.d, P.m, true, s);
+      });
+      if (st) return st;
+    }
+    *ops = GradOps{b, b + mat, b + 2 * mat};
+  } else {
+    float *w2t = static_cast<float *>(wop);
+    if (!ready) {
+      const int st = run(TTT_K_CAST, "cast", s, [&] {
+        return launch_cast(src.w1, src.w3, src.w2, nullptr, nullptr, w2t, nullptr, P.H, P.d, P.m, false, s);
+      });
+      if (st) return st;
+    }
+    *ops = GradOps{src.w1, src.w3, w2t};
+  }
+  return TTT_OK;
+}
+
+// Split partials of G over the plan's P.n tokens (k, v, eta) into `part`
+// ([P.splits][3][H][m d]).  The plan's workspace holds the pacing counters and
+// the wide-head intermediates.
+int gradient_pass(const UpdatePlan &P, const GradOps &ops, const void *k, const void *v, int64_t ld,
+                  const float *eta, int64_t eta_hs, float *part, char *ws, hipStream_t s) {
+  const size_t mat = (size_t)P.H * P.d * P.m;
+  if (P.big) {
+    BigFwdParams fp{};
+    fp.k = k, fp.v = v, fp.ld = ld, fp.eta = eta, fp.eta_hs = eta_hs;
+    fp.w1 = ops.w1, fp.w3 = ops.w3, fp.w2t = ops.w2t, fp.out = ws + P.off_inter;
+    fp.n = P.n, fp.n_pad = P.n_pad, fp.heads = P.H, fp.d = P.d, fp.m = P.m;
+    BigCtrParams cp{};
+    cp.k = k, cp.v = v, cp.ld = ld, cp.inter = ws + P.off_inter, cp.part = part;
+    cp.n = P.n, cp.n_pad = P.n_pad, cp.heads = P.H, cp.d = P.d, cp.m = P.m, cp.splits = P.splits;
+    return run(TTT_K_GRAD, "gradient", s, [&] {
+      if (P.n == 0)
+        return launch_zero_u32(reinterpret_cast<unsigned *>(part), (int)(3 * mat * (size_t)P.splits), s);
+      const hipError_t e = launch_big_fwd(fp, s);
+      return e != hipSuccess ? e : launch_big_contract(cp, s);
+    });
+  }
+  GradParams gp{};
+  gp.k = k, gp.v = v, gp.ld = ld, gp.eta = eta, gp.eta_hs = eta_hs;
+  gp.w1 = ops.w1, gp.w3 = ops.w3, gp.w2t = ops.w2t;
+  gp.part = part, gp.n = P.n, gp.nblk = P.nblk;
+  gp.heads = P.H, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
+  // the hidden tiles of a token range keep pace through these counters (see the kernel)
+  if (P.fast && P.xcd) gp.group_sync = reinterpret_cast<unsigned *>(ws + P.off_sync);
+  return run(TTT_K_GRAD, "gradient", s, [&] {
+    if (gp.group_sync) {
+      const hipError_t e = launch_zero_u32(gp.group_sync, P.H * P.splits, s);
+      if (e != hipSuccess) return e;
+    }
+    return launch_grad(gp, P.d, P.bf16, P.fast, P.grid, s);
+  });
+}
+
+// One optimiser step from the split partials `part` ([splits][3][H][m d]):
+// G = their fixed-order sum, W_out = W_src - lr NS(G) (or the norm-preserving
+// form).  write_ops: the folded path leaves the operand copies of W_out at the
+// start of the workspace.  grad_out / ns_out: optional copies of G and NS(G).
+int optimiser_step(const UpdatePlan &P, W3 src, W3o out, const float *part, int splits, float lr, bool write_ops,
+                   float *grad_out, float *ns_out, bool norm, char *ws, hipStream_t s) {
+  const size_t mat = (size_t)P.H * P.d * P.m;
+  void *const wop = ws + P.off_wop;
   float *g = reinterpret_cast<float *>(ws + P.off_g);
   float *sumsq = reinterpret_cast<float *>(ws + P.off_sumsq);
   float *x0 = reinterpret_cast<float *>(ws + P.off_x0);
@@ -234,135 +298,104 @@ int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v,
   const int slots = P.d * P.m / 4096;
   const NsShape sh{P.H, P.d, P.m};
   int st;
-  for (int t = 0; t < steps; ++t) {
-    const W3 src = t == 0 ? in : W3{out.w1, out.w3, out.w2};
-    const bool last = t == steps - 1;
-    GradParams gp{};
-    gp.k = k, gp.v = v, gp.ld = ld, gp.eta = eta, gp.eta_hs = eta_hs;
-    const bool need_cast = t == 0 ? !ops_ready : !fused;    // the folded step writes the next copies
-    if (P.bf16) {
-      __bf16 *b = static_cast<__bf16 *>(wop);
-      if (need_cast) {
-        st = run(TTT_K_CAST, "cast", s, [&] {
-          return launch_cast(src.w1, src.w3, src.w2, b, b + mat, b + 2 * mat, nullptr, P.H, P.d, P.m, true, s);
-        });
-        if (st) return st;
+  if (!g_ns_unfused) {
+    NsStepParams np{};
+    np.part = part, np.splits = splits, np.per_split = (int64_t)3 * mat;
+    np.grad_out = grad_out, np.ns_out = ns_out;
+    np.sumsq = sumsq;
+    np.x[0] = x0, np.x[1] = x1;
+    np.xt[0] = reinterpret_cast<float *>(ws + P.off_xt0), np.xt[1] = reinterpret_cast<float *>(ws + P.off_xt1);
+    np.am = am, np.bm = bm;
+    np.w1 = src.w1, np.w3 = src.w3, np.w2 = src.w2;
+    np.w1o = out.w1, np.w3o = out.w3, np.w2o = out.w2;
+    if (write_ops) {
+      if (P.bf16) {
+        __bf16 *b = static_cast<__bf16 *>(wop);
+        np.op1v = b, np.op3v = b + mat, np.op2tv = b + 2 * mat;
+      } else {
+        np.op2tv = wop;
       }
-      gp.w1 = b, gp.w3 = b + mat, gp.w2t = b + 2 * mat;
-    } else {
-      float *w2t = static_cast<float *>(wop);
-      if (need_cast) {
-        st = run(TTT_K_CAST, "cast", s, [&] {
-          return launch_cast(src.w1, src.w3, src.w2, nullptr, nullptr, w2t, nullptr, P.H, P.d, P.m, false, s);
-        });
-        if (st) return st;
-      }
-      gp.w1 = src.w1, gp.w3 = src.w3, gp.w2t = w2t;
     }
-    gp.part = part, gp.n = P.n, gp.nblk = P.nblk;
-    gp.heads = P.H, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
-    // the hidden tiles of a token range keep pace through these counters (see the kernel)
-    if (P.fast && P.xcd) gp.group_sync = reinterpret_cast<unsigned *>(ws + P.off_sync);
-    if (P.big) {
-      BigFwdParams fp{};
-      fp.k = k, fp.v = v, fp.ld = ld, fp.eta = eta, fp.eta_hs = eta_hs;
-      fp.w1 = gp.w1, fp.w3 = gp.w3, fp.w2t = gp.w2t, fp.out = ws + P.off_inter;
-      fp.n = P.n, fp.n_pad = P.n_pad, fp.heads = P.H, fp.d = P.d, fp.m = P.m;
-      BigCtrParams cp{};
-      cp.k = k, cp.v = v, cp.ld = ld, cp.inter = ws + P.off_inter, cp.part = part;
-      cp.n = P.n, cp.n_pad = P.n_pad, cp.heads = P.H, cp.d = P.d, cp.m = P.m, cp.splits = P.splits;
-      st = run(TTT_K_GRAD, "gradient", s, [&] {
-        if (P.n == 0) return launch_zero_u32(reinterpret_cast<unsigned *>(part),
-                                             (int)(3 * mat * (size_t)P.splits), s);
-        const hipError_t e = launch_big_fwd(fp, s);
-        return e != hipSuccess ? e : launch_big_contract(cp, s);
-      });
-      if (st) return st;
-    } else {
-    st = run(TTT_K_GRAD, "gradient", s, [&] {
-      if (gp.group_sync) {
-        const hipError_t e = launch_zero_u32(gp.group_sync, P.H * P.splits, s);
-        if (e != hipSuccess) return e;
-      }
-      return launch_grad(gp, P.d, P.bf16, P.fast, P.grid, s);
-    });
-    if (st) return st;
-    }
-    if (fused) {
-      NsStepParams np{};
-      np.part = part, np.splits = P.splits, np.per_split = (int64_t)3 * mat;
-      np.grad_out = last ? grad_out : nullptr, np.ns_out = last ? ns_out : nullptr;
-      np.sumsq = sumsq;
-      np.x[0] = x0, np.x[1] = x1;
-      np.xt[0] = reinterpret_cast<float *>(ws + P.off_xt0), np.xt[1] = reinterpret_cast<float *>(ws + P.off_xt1);
-      np.am = am, np.bm = bm;
-      np.w1 = src.w1, np.w3 = src.w3, np.w2 = src.w2;
-      np.w1o = out.w1, np.w3o = out.w3, np.w2o = out.w2;
-      if (!last || keep_ops) {
-        if (P.bf16) {
-          __bf16 *b = static_cast<__bf16 *>(wop);
-          np.op1v = b, np.op3v = b + mat, np.op2tv = b + 2 * mat;
-        } else {
-          np.op2tv = wop;
-        }
-      }
-      np.lr = lr, np.eps = kNsEps, np.a_coef = kNsA, np.b_coef = kNsB, np.c_coef = kNsC;
-      np.iters = kNsIters, np.heads = P.H, np.d = P.d, np.m = P.m, np.r = P.r, np.c = P.c;
-      np.norm_preserve = norm, np.wsq = wsq;
-      st = run(TTT_K_NS, "newton_schulz", s, [&] { return launch_ns_optimiser(np, P.bf16, s); });
-      if (st) return st;
-      if (norm) {
-        st = run(TTT_K_NS, "norm_rescale", s, [&] {
-          return launch_norm_rescale(out.w1, out.w3, out.w2, wsq, slots, np.op1v, np.op3v, np.op2tv, P.H, P.d, P.m,
-                                     P.bf16, s);
-        });
-        if (st) return st;
-      }
-      continue;
-    }
-    st = run(TTT_K_REDUCE, "reduce", s, [&] {
-      return launch_reduce(part, P.splits, (int64_t)3 * mat, g, last ? grad_out : nullptr, sumsq, s);
-    });
-    if (st) return st;
-    st = run(TTT_K_NS, "ns_normalize", s, [&] { return launch_ns_normalize(g, sumsq, x0, sh, kNsEps, s); });
-    if (st) return st;
-    float *x = x0, *xn = x1;
-    const int B = 3 * P.H;
-    const int64_t srr = (int64_t)P.r * P.r, src_ = (int64_t)P.r * P.c;
-    for (int it = 0; it < kNsIters; ++it) {
-      GemmBatch g1{x, x, nullptr, am, P.r, P.r, P.c, P.c, P.c, 0, P.r, 1, src_, src_, 0, srr, 1.0f, 0.0f, B};
-      GemmBatch g2{am, am, am, bm, P.r, P.r, P.r, P.r, P.r, P.r, P.r, 1, srr, srr, srr, srr, kNsC, kNsB, B};
-      GemmBatch g3{bm, x, x, xn, P.r, P.c, P.r, P.r, P.c, P.c, P.c, 0, srr, src_, src_, src_, 1.0f, kNsA, B};
-      st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g1, s); });
-      if (st) return st;
-      st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g2, s); });
-      if (st) return st;
-      st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g3, s); });
-      if (st) return st;
-      float *tmp = x;
-      x = xn;
-      xn = tmp;
-    }
-    if (norm) {
-      st = run(TTT_K_NS, "weight_sumsq", s, [&] { return launch_weight_sumsq(src.w1, src.w3, src.w2, wsq, P.H, P.d,
-                                                                              P.m, s); });
-      if (st) return st;
-    }
-    st = run(TTT_K_NS, "ns_step", s, [&] {
-      return launch_ns_step(x, src.w1, src.w3, src.w2, out.w1, out.w3, out.w2, last ? ns_out : nullptr, lr, sh, s);
-    });
+    np.lr = lr, np.eps = kNsEps, np.a_coef = kNsA, np.b_coef = kNsB, np.c_coef = kNsC;
+    np.iters = kNsIters, np.heads = P.H, np.d = P.d, np.m = P.m, np.r = P.r, np.c = P.c;
+    np.norm_preserve = norm, np.wsq = wsq;
+    st = run(TTT_K_NS, "newton_schulz", s, [&] { return launch_ns_optimiser(np, P.bf16, s); });
     if (st) return st;
     if (norm) {
-      st = run(TTT_K_NS, "weight_sumsq", s, [&] {
-        return launch_weight_sumsq(out.w1, out.w3, out.w2, wsq + 3 * P.H * slots, P.H, P.d, P.m, s);
-      });
-      if (st) return st;
       st = run(TTT_K_NS, "norm_rescale", s, [&] {
-        return launch_norm_rescale(out.w1, out.w3, out.w2, wsq, slots, nullptr, nullptr, nullptr, P.H, P.d, P.m,
+        return launch_norm_rescale(out.w1, out.w3, out.w2, wsq, slots, np.op1v, np.op3v, np.op2tv, P.H, P.d, P.m,
                                    P.bf16, s);
       });
       if (st) return st;
     }
+    return TTT_OK;
+  }
+  st = run(TTT_K_REDUCE, "reduce", s, [&] {
+    return launch_reduce(part, splits, (int64_t)3 * mat, g, grad_out, sumsq, s);
+  });
+  if (st) return st;
+  st = run(TTT_K_NS, "ns_normalize", s, [&] { return launch_ns_normalize(g, sumsq, x0, sh, kNsEps, s); });
+  if (st) return st;
+  float *x = x0, *xn = x1;
+  const int B = 3 * P.H;
+  const int64_t srr = (int64_t)P.r * P.r, src_ = (int64_t)P.r * P.c;
+  for (int it = 0; it < kNsIters; ++it) {
+    GemmBatch g1{x, x, nullptr, am, P.r, P.r, P.c, P.c, P.c, 0, P.r, 1, src_, src_, 0, srr, 1.0f, 0.0f, B};
+    GemmBatch g2{am, am, am, bm, P.r, P.r, P.r, P.r, P.r, P.r, P.r, 1, srr, srr, srr, srr, kNsC, kNsB, B};
+    GemmBatch g3{bm, x, x, xn, P.r, P.c, P.r, P.r, P.c, P.c, P.c, 0, srr, src_, src_, src_, 1.0f, kNsA, B};
+    st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g1, s); });
+    if (st) return st;
+    st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g2, s); });
+    if (st) return st;
+    st = run(TTT_K_NS, "ns_gemm", s, [&] { return launch_gemm_f32(g3, s); });
+    if (st) return st;
+    float *tmp = x;
+    x = xn;
+    xn = tmp;
+  }
+  if (norm) {
+    st = run(TTT_K_NS, "weight_sumsq", s, [&] { return launch_weight_sumsq(src.w1, src.w3, src.w2, wsq, P.H, P.d,
+                                                                            P.m, s); });
+    if (st) return st;
+  }
+  st = run(TTT_K_NS, "ns_step", s, [&] {
+    return launch_ns_step(x, src.w1, src.w3, src.w2, out.w1, out.w3, out.w2, ns_out, lr, sh, s);
+  });
+  if (st) return st;
+  if (norm) {
+    st = run(TTT_K_NS, "weight_sumsq", s, [&] {
+      return launch_weight_sumsq(out.w1, out.w3, out.w2, wsq + 3 * P.H * slots, P.H, P.d, P.m, s);
+    });
+    if (st) return st;
+    st = run(TTT_K_NS, "norm_rescale", s, [&] {
+      return launch_norm_rescale(out.w1, out.w3, out.w2, wsq, slots, nullptr, nullptr, nullptr, P.H, P.d, P.m,
+                                 P.bf16, s);
+    });
+    if (st) return st;
+  }
+  return TTT_OK;
+}
+
+// ops_ready: the operand copies of `in` are already at the start of the workspace
+// (written by the previous call's last step or by an apply cast of the same layout).
+// keep_ops: the last step leaves the operand copies of `out` there.
+// norm: the norm-preserving step (W^ = ||W|| (W - lr NS) / ||W - lr NS|| per matrix).
+int do_update(const UpdatePlan &P, W3 in, W3o out, const void *k, const void *v, int64_t ld, const float *eta,
+              int64_t eta_hs, float lr, int steps, float *grad_out, float *ns_out, char *ws, hipStream_t s,
+              bool norm, bool ops_ready = false, bool keep_ops = false) {
+  const bool fused = !g_ns_unfused;
+  float *part = reinterpret_cast<float *>(ws + P.off_part);
+  int st;
+  for (int t = 0; t < steps; ++t) {
+    const W3 src = t == 0 ? in : W3{out.w1, out.w3, out.w2};
+    const bool last = t == steps - 1;
+    // the folded step writes the next step's copies
+    GradOps ops{};
+    if ((st = prepare_operands(P, src, t == 0 ? ops_ready : fused, ws, s, &ops))) return st;
+    if ((st = gradient_pass(P, ops, k, v, ld, eta, eta_hs, part, ws, s))) return st;
+    if ((st = optimiser_step(P, src, out, part, P.splits, lr, !last || keep_ops, last ? grad_out : nullptr,
+                             last ? ns_out : nullptr, norm, ws, s)))
+      return st;
   }
   return TTT_OK;
 }
@@ -459,11 +492,11 @@ int ttt_stream_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t chun
   return TTT_OK;
 }
 
-int ttt_update_ex(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2,
-                  float *w1_out, float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv,
-                  const float *eta, int64_t eta_head_stride, int64_t n, float lr, int32_t steps, int32_t dtype,
-                  uint32_t flags, float *grad_out, float *ns_out, void *workspace, size_t workspace_bytes,
-                  void *stream) {
+// Checks shared by the update entry points: shapes, flags, weight pointers and
+// their aliasing, n, steps, lr.
+int check_update_args(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2,
+                      float *w1_out, float *w3_out, float *w2_out, int64_t n, float lr, int32_t steps, int32_t dtype,
+                      uint32_t flags) {
   int st = check_shape(heads, d, m, dtype);
   if (st) return st;
   if (flags & ~uint32_t(TTT_NORM_PRESERVE)) return fail(TTT_EINVAL, "unknown flag bits 0x%x", flags);
@@ -479,6 +512,16 @@ int ttt_update_ex(int32_t heads, int32_t d, int32_t m, const float *w1, const fl
   if (n < 0) return fail(TTT_EINVAL, "n must be >= 0");
   if (steps < 1) return fail(TTT_EINVAL, "steps must be >= 1");
   if (!std::isfinite(lr)) return fail(TTT_EINVAL, "lr must be finite");
+  return TTT_OK;
+}
+
+int ttt_update_ex(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2,
+                  float *w1_out, float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv,
+                  const float *eta, int64_t eta_head_stride, int64_t n, float lr, int32_t steps, int32_t dtype,
+                  uint32_t flags, float *grad_out, float *ns_out, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+  int st = check_update_args(heads, d, m, w1, w3, w2, w1_out, w3_out, w2_out, n, lr, steps, dtype, flags);
+  if (st) return st;
   if ((st = check_token_limits(n, ld_kv, dtype, "k/v"))) return st;
   if (n > 0) {
     if ((st = check_rows(k, ld_kv, heads, d, dtype, "k"))) return st;
@@ -491,6 +534,152 @@ int ttt_update_ex(int32_t heads, int32_t d, int32_t m, const float *w1, const fl
   return do_update(P, W3{w1, w3, w2}, W3o{w1_out, w3_out, w2_out}, k, v, ld_kv, eta, eta_head_stride, lr, steps,
                    grad_out, ns_out, static_cast<char *>(workspace), static_cast<hipStream_t>(stream),
                    (flags & TTT_NORM_PRESERVE) != 0);
+}
+
+// ------------------------------------------------------- out-of-core update
+// One copy stream per device (default priority, created on first use, kept for
+// the life of the process): host -> device copies of the next batch run on it
+// while the gradient of the current one runs on the caller's stream.
+int copy_stream(hipStream_t *out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TTT_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TTT_EUNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(TTT_EHIP, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+  }
+  *out = streams[dev];
+  return TTT_OK;
+}
+
+// Workspace of ttt_update_host: the update plan of one batch, the running G, and
+// two staging slots (K rows, V rows, the batch's rates).
+struct HostPlan {
+  UpdatePlan P;
+  size_t off_gacc, off_slot[2], slot_k, slot_e, total;
+};
+HostPlan plan_host(int H, int d, int m, int64_t batch, int64_t ld, int dtype) {
+  HostPlan h{};
+  h.P = plan_update(H, d, m, batch, dtype);
+  size_t off = h.P.total;
+  h.off_gacc = off;
+  off = align256(off + (size_t)3 * H * d * m * 4);
+  h.slot_k = align256((size_t)batch * ld * esize(dtype));
+  h.slot_e = align256((size_t)H * batch * 4);
+  for (int i = 0; i < 2; ++i) {
+    h.off_slot[i] = off;
+    off += 2 * h.slot_k + h.slot_e;
+  }
+  h.total = off;
+  return h;
+}
+
+int ttt_update_host_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t batch, int64_t ld_kv,
+                                    int32_t dtype, size_t *bytes) {
+  int st = check_shape(heads, d, m, dtype);
+  if (st) return st;
+  if (batch < 1) return fail(TTT_EINVAL, "batch must be >= 1");
+  if (ld_kv < (int64_t)heads * d) return fail(TTT_EINVAL, "ld_kv < heads*d");
+  if (!bytes) return fail(TTT_EINVAL, "bytes is null");
+  *bytes = plan_host(heads, d, m, batch, ld_kv, dtype).total;
+  return TTT_OK;
+}
+
+int ttt_update_host(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2,
+                    float *w1_out, float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv,
+                    const float *eta, int64_t eta_head_stride, int64_t n, int64_t batch, float lr, int32_t steps,
+                    int32_t dtype, uint32_t flags, float *grad_out, float *ns_out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  int st = check_update_args(heads, d, m, w1, w3, w2, w1_out, w3_out, w2_out, n, lr, steps, dtype, flags);
+  if (st) return st;
+  if (batch < 1) return fail(TTT_EINVAL, "batch must be >= 1");
+  if ((st = check_token_limits(batch, ld_kv, dtype, "k/v"))) return st;
+  if (ld_kv < (int64_t)heads * d) return fail(TTT_EINVAL, "ld_kv (%lld) < heads*d", (long long)ld_kv);
+  if ((ld_kv * (int64_t)esize(dtype)) % 16 != 0) return fail(TTT_EINVAL, "k/v rows must be 16-byte aligned");
+  if (n > 0 && (!k || !v || !eta)) return fail(TTT_EINVAL, "k, v or eta is null");
+  if (eta_head_stride < 0) return fail(TTT_EINVAL, "eta_head_stride must be >= 0");
+  const HostPlan HP = plan_host(heads, d, m, batch, ld_kv, dtype);
+  if ((st = check_ws(workspace, workspace_bytes, HP.total))) return st;
+  char *ws = static_cast<char *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool norm = (flags & TTT_NORM_PRESERVE) != 0;
+  if (n == 0)   // G = 0: the in-core path with no tokens
+    return do_update(plan_update(heads, d, m, 0, dtype), W3{w1, w3, w2}, W3o{w1_out, w3_out, w2_out}, nullptr,
+                     nullptr, ld_kv, nullptr, 0, lr, steps, grad_out, ns_out, ws, s, norm);
+  hipStream_t cs;
+  if ((st = copy_stream(&cs))) return st;
+  hipEvent_t ev[5] = {};     // ready[2], free[2], start
+  for (int i = 0; i < 5; ++i) {
+    const hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
+      return fail(TTT_EHIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+    }
+  }
+  auto hip_ok = [&](hipError_t e, const char *what) -> int {
+    if (e == hipSuccess) return TTT_OK;
+    return fail(TTT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  };
+  const size_t es = esize(dtype);
+  const size_t mat = (size_t)heads * d * m;
+  float *gacc = reinterpret_cast<float *>(ws + HP.off_gacc);
+  const int erows = eta_head_stride == 0 ? 1 : heads;
+  // the copies start after the caller's earlier work on `stream` (which may still
+  // read this workspace)
+  st = hip_ok(hipEventRecord(ev[4], s), "hipEventRecord");
+  if (!st) st = hip_ok(hipStreamWaitEvent(cs, ev[4], 0), "hipStreamWaitEvent");
+  int64_t cnt = 0;
+  for (int t = 0; t < steps && !st; ++t) {
+    const W3 src = t == 0 ? W3{w1, w3, w2} : W3{w1_out, w3_out, w2_out};
+    const bool last = t == steps - 1;
+    GradOps ops{};
+    if ((st = prepare_operands(HP.P, src, t > 0 && !g_ns_unfused, ws, s, &ops))) break;
+    for (int64_t t0 = 0; t0 < n && !st; t0 += batch, ++cnt) {
+      const int64_t len = n - t0 < batch ? n - t0 : batch;
+      const int slot = (int)(cnt & 1);
+      char *sk = ws + HP.off_slot[slot], *sv = sk + HP.slot_k;
+      float *se = reinterpret_cast<float *>(sv + HP.slot_k);
+      // copy stream: slot free (its previous batch consumed), then K, V, eta
+      if (cnt >= 2 && (st = hip_ok(hipStreamWaitEvent(cs, ev[2 + slot], 0), "hipStreamWaitEvent"))) break;
+      const size_t rows_b = (size_t)len * ld_kv * es;
+      if ((st = hip_ok(hipMemcpyAsync(sk, static_cast<const char *>(k) + t0 * ld_kv * es, rows_b,
+                                      hipMemcpyHostToDevice, cs), "hipMemcpyAsync(k)")))
+        break;
+      if ((st = hip_ok(hipMemcpyAsync(sv, static_cast<const char *>(v) + t0 * ld_kv * es, rows_b,
+                                      hipMemcpyHostToDevice, cs), "hipMemcpyAsync(v)")))
+        break;
+      if (erows == 1 || eta_head_stride >= len) {
+        const size_t spitch = (size_t)(erows > 1 ? eta_head_stride : len) * 4;
+        st = hip_ok(hipMemcpy2DAsync(se, (size_t)len * 4, eta + t0, spitch, (size_t)len * 4, erows,
+                                     hipMemcpyHostToDevice, cs), "hipMemcpy2DAsync(eta)");
+      } else {           // head rows closer than the batch: one copy per head
+        for (int hh = 0; hh < erows && !st; ++hh)
+          st = hip_ok(hipMemcpyAsync(se + (size_t)hh * len, eta + hh * eta_head_stride + t0, (size_t)len * 4,
+                                     hipMemcpyHostToDevice, cs), "hipMemcpyAsync(eta)");
+      }
+      if (st) break;
+      if ((st = hip_ok(hipEventRecord(ev[slot], cs), "hipEventRecord"))) break;
+      // compute stream: gradient of the batch, added to the running G
+      if ((st = hip_ok(hipStreamWaitEvent(s, ev[slot], 0), "hipStreamWaitEvent"))) break;
+      const UpdatePlan Pb = plan_update(heads, d, m, len, dtype);
+      float *part = reinterpret_cast<float *>(ws + Pb.off_part);
+      if ((st = gradient_pass(Pb, ops, sk, sv, ld_kv, se, erows > 1 ? len : 0, part, ws, s))) break;
+      st = run(TTT_K_REDUCE, "accumulate", s, [&] {
+        return launch_accumulate(gacc, part, Pb.splits, (int64_t)3 * mat, t0 == 0, s);
+      });
+      if (st) break;
+      st = hip_ok(hipEventRecord(ev[2 + slot], s), "hipEventRecord");
+    }
+    if (st) break;
+    st = optimiser_step(HP.P, src, W3o{w1_out, w3_out, w2_out}, gacc, 1, lr, !last, last ? grad_out : nullptr,
+                        last ? ns_out : nullptr, norm, ws, s);
+  }
+  for (int i = 0; i < 5; ++i) hipEventDestroy(ev[i]);   // released once their work completes
+  return st;
 }
 
 int ttt_update(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2, float *w1_out,

@@ -104,6 +104,10 @@ struct NsStepParams {
 };
 hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s);
 
+// acc = (first ? 0 : acc) + sum_s part[s * per_split ..] (per_split % 4 == 0), fixed order.
+hipError_t launch_accumulate(float *acc, const float *part, int splits, int64_t per_split, bool first,
+                             hipStream_t s);
+
 // Per-4096-element sums of squares of W1, W3, W2 in matrix order [3][H] (d*m/4096
 // slots per matrix), written to out[0 .. 3H * slots).
 hipError_t launch_weight_sumsq(const float *w1, const float *w3, const float *w2, float *out, int heads, int d,

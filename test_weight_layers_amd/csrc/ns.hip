@@ -40,6 +40,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ p
   if (threadIdx.x == 0) sumsq[blockIdx.x] = red[0];
 }
 
+// acc = (first ? 0 : acc) + sum over splits of part, in split order (deterministic).
+__global__ __launch_bounds__(256) void accumulate_kernel(float *__restrict__ acc, const float *__restrict__ part,
+                                                         int splits, int64_t per_split, int first) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= per_split) return;
+  f32x4 v = first ? f32x4{0, 0, 0, 0} : *reinterpret_cast<const f32x4 *>(acc + i);
+  for (int s = 0; s < splits; ++s) v += *reinterpret_cast<const f32x4 *>(part + (int64_t)s * per_split + i);
+  *reinterpret_cast<f32x4 *>(acc + i) = v;
+}
+
 // Matrix b (0 .. 3H-1): j = b / H selects G1, G3, G2; G1/G3 are [m][d], G2 [d][m].
 // X_b is [r][c] with r = min(d, m), c = max(d, m): the transpose of G_b when G_b
 // has more rows than columns.
@@ -514,6 +524,14 @@ hipError_t ns_optimiser_impl(const NsStepParams &p, hipStream_t s) {
 
 hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s) {
   return bf16 ? ns_optimiser_impl<__bf16>(p, s) : ns_optimiser_impl<float>(p, s);
+}
+
+hipError_t launch_accumulate(float *acc, const float *part, int splits, int64_t per_split, bool first,
+                             hipStream_t s) {
+  const int64_t blocks = (per_split / 4 + 255) / 256;
+  hipLaunchKernelGGL(accumulate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, acc, part, splits, per_split,
+                     first ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_weight_sumsq(const float *w1, const float *w3, const float *w2, float *out, int heads, int d,

@@ -22,7 +22,7 @@ OPT_FORCE_GENERAL, OPT_SPLITS, OPT_NS_UNFUSED = 0, 1, 2
 KERNEL_KINDS = ("conv", "cast", "grad", "reduce", "ns", "apply", "gate")
 NORM_PRESERVE = 1
 EXPORTS = ("ttt_last_error", "ttt_update_workspace_bytes", "ttt_apply_workspace_bytes", "ttt_update",
-           "ttt_update_ex", "ttt_apply", "ttt_output_gate", "ttt_shortconv2d", "ttt_stream_workspace_bytes",
+           "ttt_update_ex", "ttt_update_host_workspace_bytes", "ttt_update_host", "ttt_apply", "ttt_output_gate", "ttt_shortconv2d", "ttt_stream_workspace_bytes",
            "ttt_stream", "ttt_stream_ex", "ttt_set_option", "ttt_profile_enable", "ttt_profile_reset",
            "ttt_profile_read")
 
@@ -52,6 +52,9 @@ def load() -> ctypes.CDLL:
                                       i32, vp, vp, vp, sz, vp]),
         "ttt_update_ex": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, f32,
                                          i32, i32, u32, vp, vp, vp, sz, vp]),
+        "ttt_update_host_workspace_bytes": (ctypes.c_int, [i32, i32, i32, i64, i64, i32, szp]),
+        "ttt_update_host": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, i64,
+                                           f32, i32, i32, u32, vp, vp, vp, sz, vp]),
         "ttt_output_gate": (ctypes.c_int, [i32, vp, i64, vp, vp, f32, vp, i64, i64, i32, vp]),
         "ttt_stream_ex": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, i64, vp, i64, i64,
                                          i64, f32, i32, i32, u32, vp, sz, vp]),
@@ -174,6 +177,46 @@ def update(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: tor
                                 eta.data_ptr(), ehs, n, float(lr), int(steps), code, flags, _ptr(grad_out),
                                 _ptr(ns_out), _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                 _stream()))
+    return tuple(out)
+
+
+def update_host_workspace_bytes(heads: int, d: int, m: int, batch: int, ld: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t()
+    code = TTT_BF16 if dtype == torch.bfloat16 else TTT_F32
+    _check(load().ttt_update_host_workspace_bytes(heads, d, m, batch, ld, code, ctypes.byref(out)))
+    return out.value
+
+
+def update_host(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor, lr: float,
+                steps: int = 1, batch: int = 65536, out: Optional[Sequence[torch.Tensor]] = None,
+                grad_out: Optional[torch.Tensor] = None, ns_out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, norm_preserve: bool = False):
+    """Fast-weight update with K, V, eta in host memory (pinned for overlap), streamed in batches."""
+    H, d, m = _weights(w)
+    if out is None:
+        out = tuple(torch.empty_like(x) for x in w)
+    _weights(out)
+    n = k.shape[0]
+    code = _dtype_code(k)
+    if k.is_cuda or v.is_cuda or eta.is_cuda:
+        raise ValueError("update_host takes k, v and eta in host memory")
+    if v.dtype != k.dtype or v.shape != k.shape or v.stride() != k.stride() or k.dim() != 2 or k.stride(1) != 1:
+        raise ValueError("k and v must be 2-D host tensors sharing dtype, shape and strides")
+    if eta.dtype != torch.float32:
+        raise ValueError("eta must be float32")
+    ehs = eta.stride(0) if eta.dim() == 2 else 0
+    for t, name in ((grad_out, "grad_out"), (ns_out, "ns_out")):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != 3 * H * d * m or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of 3*H*m*d elements")
+    ld = k.stride(0)
+    need = update_host_workspace_bytes(H, d, m, batch, ld, k.dtype)
+    if workspace is None:
+        workspace = _workspace(need, w[0].device)
+    flags = NORM_PRESERVE if norm_preserve else 0
+    _check(load().ttt_update_host(H, d, m, *map(_ptr, w), *map(_ptr, out), k.data_ptr(), v.data_ptr(), ld,
+                                  eta.data_ptr(), ehs, n, batch, float(lr), int(steps), code, flags, _ptr(grad_out),
+                                  _ptr(ns_out), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                  _stream()))
     return tuple(out)
 
 

@@ -127,3 +127,24 @@ def test_update_ex_stream_ex_and_gate_argument_errors(lib):
     assert st == -1
     # n = 0 launches nothing and succeeds
     assert lib.ttt_output_gate(64, None, 64, None, None, 1e-6, None, 64, 0, ttt.TTT_BF16, None) == 0
+
+
+def test_update_host_argument_errors(lib):
+    fake = 1 << 20
+    st, nb = _ws(lib, "ttt_update_host_workspace_bytes", 4, 256, 512, 4096, 1024, ttt.TTT_BF16)
+    assert st == 0 and nb > 2 * 4096 * 1024 * 2 * 2          # two staging slots of K and V at least
+    st, _ = _ws(lib, "ttt_update_host_workspace_bytes", 4, 256, 512, 0, 1024, ttt.TTT_BF16)
+    assert st == -1
+    # batch < 1, null host rows, unaligned rows: rejected before any copy or launch
+    st = lib.ttt_update_host(1, 64, 128, fake, fake * 2, fake * 3, fake * 4, fake * 5, fake * 6, fake, fake, 64,
+                             fake, 0, 10, 0, 0.01, 1, ttt.TTT_F32, 0, None, None, fake, 1 << 30, None)
+    assert st == -1 and b"batch" in lib.ttt_last_error()
+    st = lib.ttt_update_host(1, 64, 128, fake, fake * 2, fake * 3, fake * 4, fake * 5, fake * 6, None, fake, 64,
+                             fake, 0, 10, 5, 0.01, 1, ttt.TTT_F32, 0, None, None, fake, 1 << 30, None)
+    assert st == -1 and b"null" in lib.ttt_last_error()
+    st = lib.ttt_update_host(1, 64, 128, fake, fake * 2, fake * 3, fake * 4, fake * 5, fake * 6, fake, fake, 66,
+                             fake, 0, 10, 5, 0.01, 1, ttt.TTT_BF16, 0, None, None, fake, 1 << 30, None)
+    assert st == -1 and b"aligned" in lib.ttt_last_error()
+    st = lib.ttt_update_host(1, 64, 128, fake, fake * 2, fake * 3, fake * 4, fake * 5, fake * 6, fake, fake, 64,
+                             fake, 0, 10, 5, 0.01, 1, ttt.TTT_F32, 0, None, None, fake, 16, None)
+    assert st == -3

@@ -1,0 +1,86 @@
+"""Out-of-core update (VGG-T3 关键发现 2: minibatch gradient accumulation with the
+tokens offloaded to the CPU): K, V and eta stay in host memory and are streamed
+in batches; the running G is the sum of the batches' gradients.
+
+Checked against the in-core update on the same tokens and against the fp64
+oracle (the layer's tolerance: 1e-4 fp32, 2e-2 bf16), per head and per matrix on
+G, NS(G) and the step W^ - W.  The two paths sum the token gradients in a
+different fp32 order (about 1e-6 relative); with bf16 operands a later inner step
+casts the two slightly different W to bf16, and the elements whose rounding flips
+move G by up to a bf16 ulp, so the cross-path bar is 1e-5 for fp32 and 1e-3 for
+bf16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, cfg_like, rel
+from test_weight_layers_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from test_weight_layers_amd import ttt
+    ttt.load()
+    ttt.set_option(ttt.OPT_FORCE_GENERAL, 0)
+    ttt.set_option(ttt.OPT_SPLITS, 0)
+    ttt.set_option(ttt.OPT_NS_UNFUSED, 0)
+
+
+CASES = {
+    # name: (config, tokens, batch, lr, steps, norm-preserving, pinned, shared eta)
+    "vggt-bf16-2step": (cfg_like("c4", heads=2), 2000, 700, 0.01, 2, False, True, False),
+    "c1-fp32": (cfg_like("c1"), 256, 100, 0.01, 1, False, True, False),
+    "d768-bf16": (cfg_like("c2"), 1300, 500, 0.01, 1, False, True, False),
+    "norm-bf16-2step": (cfg_like("c4", heads=2, d=128, m=256), 1500, 400, 0.3, 2, True, True, False),
+    "one-batch": (cfg_like("c4", heads=1), 900, 5000, 0.01, 1, False, True, False),
+    "pageable-shared-eta": (cfg_like("c4", heads=2, d=64, m=128), 1000, 333, 0.01, 1, False, False, True),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_update_host_matches_in_core_and_oracle(case):
+    from test_weight_layers_amd import ttt
+    cfg, n, batch, lr, steps, norm, pinned, shared = CASES[case]
+    H, d, m = cfg.heads, cfg.d, cfg.m
+    inp = synth.make_inputs(cfg, n=n, nq_extra=0)
+    eta = inp.eta[0].clone() if shared else inp.eta
+    dv = synth.to_device(inp, "cuda")
+    w = (dv.w1, dv.w3, dv.w2)
+    host = lambda t: t.contiguous().pin_memory() if pinned else t.contiguous()
+    kh, vh, eh = host(inp.k), host(inp.v), host(eta)
+    mat = H * m * d
+    g_dev, ns_dev = torch.empty(3 * mat, device="cuda"), torch.empty(3 * mat, device="cuda")
+    g_host, ns_host = torch.empty_like(g_dev), torch.empty_like(g_dev)
+    w_dev = ttt.update(w, dv.k, dv.v, eta.cuda(), lr, steps, grad_out=g_dev, ns_out=ns_dev, norm_preserve=norm)
+    w_host = ttt.update_host(w, kh, vh, eh, lr, steps, batch=batch, grad_out=g_host, ns_out=ns_host,
+                             norm_preserve=norm)
+    w_again = ttt.update_host(w, kh, vh, eh, lr, steps, batch=batch, norm_preserve=norm)
+    torch.cuda.synchronize()
+    for a, b in zip(w_host, w_again):           # deterministic for a given batch
+        assert torch.equal(a, b)
+    f = synth.as_f64
+    split = lambda t: (f(t[:mat].view(H, m, d)), f(t[mat:2 * mat].view(H, m, d)), f(t[2 * mat:].view(H, d, m)))
+    w0 = [f(t) for t in (inp.w1, inp.w3, inp.w2)]
+    eta_ref = np.broadcast_to(f(eta), (H, n)) if shared else f(eta)
+    w_ref, g_ref, ns_ref = oracle.update(*w0, f(inp.k), f(inp.v), eta_ref, lr, steps, norm_preserve=norm)
+    tol = TOL[cfg.dtype]
+    same = 1e-5 if cfg.dtype == "f32" else 1e-3
+    worst = {}
+    for j, (gh, gd, nh, nd, whh, wdd) in enumerate(zip(split(g_host), split(g_dev), split(ns_host), split(ns_dev),
+                                                       map(f, w_host), map(f, w_dev))):
+        for h in range(H):
+            assert rel(gh[h], gd[h]) <= same and rel(nh[h], nd[h]) <= same
+            assert rel(whh[h] - w0[j][h], wdd[h] - w0[j][h]) <= same
+            worst[f"G{j}[h{h}]"] = rel(gh[h], g_ref[j][h])
+            worst[f"NS{j}[h{h}]"] = rel(nh[h], ns_ref[j][h])
+            worst[f"dW{j}[h{h}]"] = rel(whh[h] - w0[j][h], w_ref[j][h] - w0[j][h])
+    top = max(worst, key=worst.get)
+    print(f"update_host {case}: worst vs oracle {top} = {worst[top]:.3e}")
+    bad = {k: v for k, v in worst.items() if not v <= tol}
+    assert not bad, bad
