@@ -143,11 +143,22 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
       hf[t] = pack8<__bf16>(hv);
     }
     // O^T[d][tok] += W2[d][chunk] H^T
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    // the transposing reads run kRing column blocks ahead of their MFMAs (a read's
+    // latency is longer than the two MFMAs it feeds)
+    constexpr int kRing = 8;
+    bf16x4 wlo[kRing], whi[kRing];
+    auto rd_w2 = [&](int dt) __attribute__((always_inline)) {
       int b0 = base_b[0], b1 = base_b[1];
       asm volatile("" : "+v"(b0), "+v"(b1));
-      const bf16x8 w2f = cat8(lds_read_tr16(base + (b0 ^ (32 * dt))), lds_read_tr16(base + (b1 ^ (32 * dt))));
+      wlo[dt % kRing] = lds_read_tr16(base + (b0 ^ (32 * dt)));
+      whi[dt % kRing] = lds_read_tr16(base + (b1 ^ (32 * dt)));
+    };
+#pragma unroll
+    for (int q = 0; q < kRing - 1 && q < DT; ++q) rd_w2(q);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      if (dt + kRing - 1 < DT) rd_w2(dt + kRing - 1);
+      const bf16x8 w2f = cat8(wlo[dt % kRing], whi[dt % kRing]);
       acc[dt][0] = mma(w2f, hf[0], acc[dt][0]);
       acc[dt][1] = mma(w2f, hf[1], acc[dt][1]);
     }
