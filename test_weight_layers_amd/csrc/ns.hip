@@ -211,12 +211,19 @@ constexpr int kT = 64;        // output tile
 constexpr int kKc = 64;       // K chunk
 constexpr int kLdsW = kKc + 4;
 
+constexpr int kLdsH = kKc + 8;   // bf16 row of a split tile: 144 bytes, 16 rows at one
+                                 // 16-byte column hit 16 distinct bank groups
+
 struct NsSmem {
   union {
     struct {
       float a[2][kT][kLdsW];
       float b[2][kT][kLdsW];
     } g;
+    struct {                     // bf16 hi / lo parts of the same chunks
+      __bf16 ah[2][kT][kLdsH], al[2][kT][kLdsH];
+      __bf16 bh[2][kT][kLdsH], bl[2][kT][kLdsH];
+    } h;
     float tr[kT][kT + 1];
   };
   float red[256];
@@ -261,6 +268,72 @@ __device__ __forceinline__ void tile_nt(const float *__restrict__ P, int ldp, co
       acc[0][1] = mma(a0, b1, acc[0][1]);
       acc[1][0] = mma(a1, b0, acc[1][0]);
       acc[1][1] = mma(a1, b1, acc[1][1]);
+    }
+  }
+}
+
+// tile_nt with each fp32 operand split into bf16 hi + lo (x = hi + lo to about 16
+// significant bits) and the product taken as hi*hi + hi*lo + lo*hi on bf16 MFMA,
+// fp32 accumulation: about 2e-5 relative error on Newton-Schulz's output (fp32
+// products give 2e-6) for a fifth of the fp32-MFMA cycles.
+__device__ __forceinline__ void split4(const f32x4 v, __bf16 *hi, __bf16 *lo) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    h[z] = (__bf16)v[z];
+    l[z] = (__bf16)(v[z] - (float)h[z]);
+  }
+  *reinterpret_cast<bf16x4 *>(hi) = h;
+  *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+__device__ __forceinline__ void tile_nt_split(const float *__restrict__ P, int ldp, const float *__restrict__ Q,
+                                              int ldq, int K, NsSmem &sm, f32x4 acc[2][2]) {
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
+  const int lr = t >> 4, lc = (t & 15) * 4;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x4{0, 0, 0, 0};
+  f32x4 pa[4], pb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 16 * u) * ldp + lc);
+    pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 16 * u) * ldq + lc);
+  }
+  const int nk = K / kKc;
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      split4(pa[u], &sm.h.ah[buf][lr + 16 * u][lc], &sm.h.al[buf][lr + 16 * u][lc]);
+      split4(pb[u], &sm.h.bh[buf][lr + 16 * u][lc], &sm.h.bl[buf][lr + 16 * u][lc]);
+    }
+    __syncthreads();
+    if (kc + 1 < nk) {
+      const int k0 = (kc + 1) * kKc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 16 * u) * ldp + k0 + lc);
+        pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 16 * u) * ldq + k0 + lc);
+      }
+    }
+    const int ra = (w >> 1) * 32 + li, rb = (w & 1) * 32 + li;
+#pragma unroll
+    for (int kk = 0; kk < kKc; kk += 32) {
+      bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ah[i] = ld8(&sm.h.ah[buf][ra + 16 * i][kk + 8 * g]);
+        al[i] = ld8(&sm.h.al[buf][ra + 16 * i][kk + 8 * g]);
+        bh[i] = ld8(&sm.h.bh[buf][rb + 16 * i][kk + 8 * g]);
+        bl[i] = ld8(&sm.h.bl[buf][rb + 16 * i][kk + 8 * g]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mma(al[i], bh[j], acc[i][j]);
+          acc[i][j] = mma(ah[i], bl[j], acc[i][j]);
+          acc[i][j] = mma(ah[i], bh[j], acc[i][j]);
+        }
     }
   }
 }
@@ -352,9 +425,17 @@ __global__ __launch_bounds__(256) void ns_tile_kernel(NsStepParams p, int cur, i
     alpha = PH == 0 ? s * s : s;
   }
   f32x4 acc[2][2];
-  if (PH == 0) tile_nt(X + (int64_t)ti * kT * c, c, X + (int64_t)tj * kT * c, c, c, sm, acc);
-  if (PH == 1) tile_nt(A + (int64_t)ti * kT * r, r, A + (int64_t)tj * kT * r, r, r, sm, acc);
-  if (PH >= 2) tile_nt(Bm + (int64_t)ti * kT * r, r, XT + (int64_t)tj * kT * r, r, r, sm, acc);
+  // bf16 mode: split-bf16 products; fp32 mode: fp32 MFMA
+  constexpr bool split = sizeof(T) == 2;
+  auto prod = [&](const float *P, int ldp, const float *Q, int ldq, int K) __attribute__((always_inline)) {
+    if constexpr (split)
+      tile_nt_split(P, ldp, Q, ldq, K, sm, acc);
+    else
+      tile_nt(P, ldp, Q, ldq, K, sm, acc);
+  };
+  if (PH == 0) prod(X + (int64_t)ti * kT * c, c, X + (int64_t)tj * kT * c, c, c);
+  if (PH == 1) prod(A + (int64_t)ti * kT * r, r, A + (int64_t)tj * kT * r, r, r);
+  if (PH >= 2) prod(Bm + (int64_t)ti * kT * r, r, XT + (int64_t)tj * kT * r, r, r);
   const int hj = b / H, h = b % H;
   const bool tr = (hj < 2 ? m : d) > (hj < 2 ? d : m);
   float ssw = 0.0f, ssd = 0.0f;      // norm-preserving form: sums of squares of W and W - lr NS

@@ -7,8 +7,8 @@ oracle (the layer's tolerance: 1e-4 fp32, 2e-2 bf16), per head and per matrix on
 G, NS(G) and the step W^ - W.  The two paths sum the token gradients in a
 different fp32 order (about 1e-6 relative); with bf16 operands a later inner step
 casts the two slightly different W to bf16, and the elements whose rounding flips
-move G by up to a bf16 ulp, so the cross-path bar is 1e-5 for fp32 and 1e-3 for
-bf16.
+move G by up to a bf16 ulp, which Newton-Schulz passes on with a gain of a few.
+The cross-path bar is 1e-5 for fp32, 1e-3 for one bf16 step and 1e-2 for two.
 """
 import numpy as np
 import pytest
@@ -70,7 +70,7 @@ def test_update_host_matches_in_core_and_oracle(case):
     eta_ref = np.broadcast_to(f(eta), (H, n)) if shared else f(eta)
     w_ref, g_ref, ns_ref = oracle.update(*w0, f(inp.k), f(inp.v), eta_ref, lr, steps, norm_preserve=norm)
     tol = TOL[cfg.dtype]
-    same = 1e-5 if cfg.dtype == "f32" else 1e-3
+    same = 1e-5 if cfg.dtype == "f32" else (1e-3 if steps == 1 else 1e-2)
     worst = {}
     for j, (gh, gd, nh, nd, whh, wdd) in enumerate(zip(split(g_host), split(g_dev), split(ns_host), split(ns_dev),
                                                        map(f, w_host), map(f, w_dev))):
