@@ -11,9 +11,9 @@
 // 64 (w % 4) .. +64 and channels 128 (w / 4) .. +128 (4 x 8 MFMA 16x16 tiles),
 // so every staged byte feeds 128 multiply-adds: the L2 -> LDS supply of about
 // 12-18 bytes per clock per CU, not the MFMA rate, is what a narrower tile hits.
-// The reduction runs over C in chunks of 32 elements (one MFMA step), DMA'd from
-// global memory straight into a ring of LDS stages (4 x 32 KB for bf16, 2 x 64 KB
-// for fp32), NST - 1 chunks ahead of the one being multiplied.  The RMS sums of
+// The reduction runs over C in chunks of 128 bytes per row (64 bf16 / 32 fp32),
+// DMA'd from global memory straight into two 64 KB LDS stages, one chunk ahead
+// of the one being multiplied.  The RMS sums of
 // squares come from the O' fragments the channel-0 waves already hold.
 #include "common.h"
 #include "kernels.h"
@@ -25,38 +25,38 @@ constexpr int kGateTok = 256;     // tokens per workgroup
 constexpr int kGateCh = 256;      // output channels per workgroup
 
 template <typename T> struct GateGeo {
-  static constexpr int kRowB = 32 * (int)sizeof(T);     // one chunk of a row: 64 / 128 bytes
+  static constexpr int kRowB = 128;                     // one chunk of a row: a whole cache line
+  static constexpr int kEpc = kRowB / (int)sizeof(T);   // reduction elements per chunk: 64 / 32
+  static constexpr int kKs = kEpc / 32;                 // MFMA k-steps per chunk
   static constexpr int kPieces = kRowB / 16;            // 16-byte pieces per row
   static constexpr int kRowsPerKb = 1024 / kRowB;       // rows per 1 KB DMA piece
   static constexpr int kStageA = kGateTok * kRowB;
   static constexpr int kStage = kStageA + kGateCh * kRowB;
-  static constexpr int kNst = sizeof(T) == 2 ? 4 : 2;   // ring depth
+  static constexpr int kNst = 2;                        // ring depth
   static constexpr int kDmaA = kStageA / 1024 / 8;      // 1 KB DMAs per wave per stage (A part)
   static constexpr int kDmaB = kGateCh * kRowB / 1024 / 8;
   static constexpr int kDma = kDmaA + kDmaB;
 };
 
 // Piece c of staged row r sits at position c ^ swizzle(r).  Fragment reads take
-// 16 consecutive rows at one piece (16 lanes per LDS cycle for 16-byte reads).
-// 64-byte rows (4 per 256-byte bank line): swz_64 spreads rows R..R+15 over 16
-// positions.  128-byte rows: rows r and r + 2q collide without a swizzle, so the
-// piece index is XORed with r / 2.
-template <typename T> __device__ __forceinline__ int gate_swz(int r);
-template <> __device__ __forceinline__ int gate_swz<__bf16>(int r) { return swz_64(r); }
-template <> __device__ __forceinline__ int gate_swz<float>(int r) { return (r >> 1) & 7; }
+// 16 consecutive rows at one piece (16 lanes per LDS cycle for 16-byte reads);
+// with 128-byte rows, rows r and r + 2q collide without a swizzle, so the piece
+// index is XORed with r / 2.  Whole 128-byte rows per chunk make every DMA
+// instruction fetch 8 full cache lines (64-byte halves would touch 16).
+template <typename T> __device__ __forceinline__ int gate_swz(int r) { return (r >> 1) & 7; }
 template <typename T> __device__ __forceinline__ int gate_slot(int r, int c) {
   return r * GateGeo<T>::kRowB + ((c ^ gate_swz<T>(r)) << 4);
 }
 
-// lane group g's 8 reduction elements 8g .. 8g+7 of staged row r
+// lane group g's 8 reduction elements 32 ks + 8g .. +8 of staged row r
 template <typename T> __device__ __forceinline__ typename FragOf<T>::type gate_frag(const unsigned char *s, int r,
-                                                                                   int g);
-template <> __device__ __forceinline__ bf16x8 gate_frag<__bf16>(const unsigned char *s, int r, int g) {
-  return *reinterpret_cast<const bf16x8 *>(s + gate_slot<__bf16>(r, g));
+                                                                                   int ks, int g);
+template <> __device__ __forceinline__ bf16x8 gate_frag<__bf16>(const unsigned char *s, int r, int ks, int g) {
+  return *reinterpret_cast<const bf16x8 *>(s + gate_slot<__bf16>(r, 4 * ks + g));
 }
-template <> __device__ __forceinline__ f32x8 gate_frag<float>(const unsigned char *s, int r, int g) {
-  const f32x4 lo = *reinterpret_cast<const f32x4 *>(s + gate_slot<float>(r, 2 * g));
-  const f32x4 hi = *reinterpret_cast<const f32x4 *>(s + gate_slot<float>(r, 2 * g + 1));
+template <> __device__ __forceinline__ f32x8 gate_frag<float>(const unsigned char *s, int r, int ks, int g) {
+  const f32x4 lo = *reinterpret_cast<const f32x4 *>(s + gate_slot<float>(r, 8 * ks + 2 * g));
+  const f32x4 hi = *reinterpret_cast<const f32x4 *>(s + gate_slot<float>(r, 8 * ks + 2 * g + 1));
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -151,21 +151,24 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
 
   auto compute = [&](const unsigned char *stage) __attribute__((always_inline)) {
     if (!active) return;
-    typename FragOf<T>::type fa[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) fa[a] = gate_frag<T>(stage, 64 * wr + 16 * a + li, g);
+    for (int ks = 0; ks < G::kKs; ++ks) {
+      typename FragOf<T>::type fa[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const typename FragOf<T>::type fb = gate_frag<T>(stage + G::kStageA, 128 * wc + 16 * e + li, g);
+      for (int a = 0; a < 4; ++a) fa[a] = gate_frag<T>(stage, 64 * wr + 16 * a + li, ks, g);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc[a][e] = mma(fa[a], fb, acc[a][e]);
-    }
-    if (wc == 0) {
+      for (int e = 0; e < 8; ++e) {
+        const typename FragOf<T>::type fb = gate_frag<T>(stage + G::kStageA, 128 * wc + 16 * e + li, ks, g);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) ss[a] += frag_sumsq(fa[a]);
+        for (int a = 0; a < 4; ++a) acc[a][e] = mma(fa[a], fb, acc[a][e]);
+      }
+      if (wc == 0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) ss[a] += frag_sumsq(fa[a]);
+      }
     }
   };
-  const int nk = C / 32;
+  const int nk = C / G::kEpc;
   // one chunk: wait for its stage (the later chunks' DMAs may stay in flight),
   // barrier, refill the stage read one chunk ago with chunk kc + NST - 1, multiply
   auto step = [&](int kc, const unsigned char *cur, unsigned char *refill) __attribute__((always_inline)) {
@@ -210,8 +213,8 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
     // consecutive channels of a row with 16-byte loads of O' and 16-byte stores.
     // Tile column c of row r sits at c ^ (16 ((r / 4) % 4)), so the four row
     // groups of a 2-byte store wave land on distinct banks.
-    auto zrow = [&](int blk) __attribute__((always_inline)) -> __bf16 * {
-      return reinterpret_cast<__bf16 *>(blk == 0 ? st0 : blk == 1 ? st1 : blk == 2 ? st2 : st3);
+    auto zrow = [&](int blk) __attribute__((always_inline)) -> __bf16 * {   // 64 rows of 512 bytes
+      return reinterpret_cast<__bf16 *>((blk < 2 ? st0 : st1) + (blk & 1) * 64 * 512);
     };
     __syncthreads();                  // every wave is done with the ring
     if (active) {
