@@ -224,3 +224,34 @@ def test_stream_against_oracle(kind):
             dw_ref = w_ref[j][h] - f((inp.w1, inp.w3, inp.w2)[j][h])
             dw = w[j][h].double().cpu().numpy() - f((inp.w1, inp.w3, inp.w2)[j][h])
             assert rel(dw, dw_ref) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gradient_token_order_and_shard_additivity(dtype):
+    # one gradient sees every token in any order (ZipMap 关键设计 1; Scal3R 方案1), and it
+    # is a sum over token shards (Scal3R 方案2: the multi-GPU all-reduce, here emulated by
+    # shards summed on one device): both hold up to the fp32 order of the sum
+    from test_weight_layers_amd import ttt
+    cfg = cfg_like("c4", heads=2, d=128, m=256, dtype=dtype)
+    n = 3000
+    inp = synth.to_device(synth.make_inputs(cfg, n=n, nq_extra=0), "cuda")
+    H, d, m = cfg.heads, cfg.d, cfg.m
+    w = (inp.w1, inp.w3, inp.w2)
+    mat = 3 * H * m * d
+    g_full = torch.empty(mat, device="cuda")
+    ttt.update(w, inp.k, inp.v, inp.eta, 0.0, 1, grad_out=g_full)
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(3)).cuda()
+    g_perm = torch.empty_like(g_full)
+    ttt.update(w, inp.k[perm].contiguous(), inp.v[perm].contiguous(), inp.eta[:, perm].contiguous(), 0.0, 1,
+               grad_out=g_perm)
+    g_sum = torch.zeros_like(g_full)
+    for t0, t1 in ((0, 1000), (1000, 1777), (1777, 3000)):
+        g_s = torch.empty_like(g_full)
+        ttt.update(w, inp.k[t0:t1], inp.v[t0:t1], inp.eta[:, t0:t1].contiguous(), 0.0, 1, grad_out=g_s)
+        g_sum += g_s
+    torch.cuda.synchronize()
+    ref = g_full.double()
+    tol = 1e-5 if dtype == "f32" else 1e-4
+    for got in (g_perm, g_sum):
+        err = float((got.double() - ref).norm() / ref.norm())
+        assert err <= tol, err
