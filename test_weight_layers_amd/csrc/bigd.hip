@@ -49,20 +49,21 @@ __device__ __forceinline__ int64_t xcd_work_item(int64_t total) {
 
 // ------------------------------------------------------------------ NT tiles
 // C[i][j] = sum_k A[i][k] B[j][k], every operand row k-contiguous in HBM.  A
-// workgroup (8 waves, 4 x 2) stages NA "A" operands of TM rows and NB "B"
-// operands of TN rows, 32 reduction elements (64 bytes) per row, and multiplies
-// NP (A, B) pairs into NP accumulator sets.  Stages are DMA'd 1 KB (16 rows) per
-// wave instruction into a ring of NST stages, NST - 1 chunks ahead.
-template <int NA_, int NB_, int TM_, int TN_, int NST_>
+// workgroup (WR x WC waves) stages NA "A" operands of TM rows and NB "B" operands
+// of TN rows, 32 reduction elements (64 bytes) per row, and multiplies NP (A, B)
+// pairs into NP accumulator sets.  Stages are DMA'd 1 KB (16 rows) per wave
+// instruction into a ring of NST stages, NST - 1 chunks ahead.
+template <int NA_, int NB_, int TM_, int TN_, int NST_, int WR_ = 4, int WC_ = 2>
 struct NtGeo {
-  static constexpr int NA = NA_, NB = NB_, TM = TM_, TN = TN_, NST = NST_;
+  static constexpr int NA = NA_, NB = NB_, TM = TM_, TN = TN_, NST = NST_, WR = WR_, WC = WC_;
+  static constexpr int kWaves = WR * WC, kThreads = 64 * kWaves;
   static constexpr int kRows = NA * TM + NB * TN;
   static constexpr int kStage = kRows * 64;
-  static constexpr int kPPW = kStage / 1024 / 8;     // DMA pieces per wave per stage
-  static constexpr int WM = TM / 4, WN = TN / 2;     // wave tile
-  static constexpr int FM = WM / 16, FN = WN / 16;   // MFMA tiles per wave
-  static_assert((kStage / 1024) % 8 == 0, "stage must split evenly over 8 waves");
-  static_assert(TM % 64 == 0 && TN % 32 == 0, "tile shape");
+  static constexpr int kPPW = kStage / 1024 / kWaves;  // DMA pieces per wave per stage
+  static constexpr int WM = TM / WR, WN = TN / WC;     // wave tile
+  static constexpr int FM = WM / 16, FN = WN / 16;     // MFMA tiles per wave
+  static_assert((kStage / 1024) % kWaves == 0, "stage must split evenly over the waves");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "tile shape");
 };
 
 // 16-byte piece c (0..3) of staged 64-byte row r sits at c ^ swz_64(r): 16 lanes
@@ -144,9 +145,12 @@ __device__ __forceinline__ int st128(int r, int c) { return r * 128 + (c ^ (16 *
 __device__ __forceinline__ int st256(int r, int c) { return r * 256 + (c ^ (16 * ((r >> 2) & 3))); }
 
 // ------------------------------------------------------- gradient, forward
+// 8 waves, two per SIMD (a 4-wave layout with 64 x 64 wave tiles and AGPR
+// accumulators needs a third fewer fragment reads per MFMA but measured 13% slower:
+// one wave per SIMD leaves its read latencies exposed)
 using FwdGeo = NtGeo<2, 3, 128, 128, 3>;   // A: K, V tokens; B: W1, W3, W2^T hidden rows
 
-__global__ __launch_bounds__(512) void big_fwd_kernel(BigFwdParams p) {
+__global__ __launch_bounds__(FwdGeo::kThreads) void big_fwd_kernel(BigFwdParams p) {
   using G = FwdGeo;
   __shared__ __attribute__((aligned(1024))) unsigned char st0[G::kStage];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[G::kStage];
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(512) void big_fwd_kernel(BigFwdParams p) {
   const int64_t tok0 = tt * G::TM;
   const int u0 = tu * G::TN;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 4, li = l & 15;
-  const int wr = w & 3, wc = w >> 2;
+  const int wr = w % G::WR, wc = w / G::WR;
   const int d = p.d, m = p.m;
   const int64_t mat = (int64_t)m * d;
 
@@ -212,13 +216,14 @@ __global__ __launch_bounds__(512) void big_fwd_kernel(BigFwdParams p) {
       }
     }
   __syncthreads();
-  // 3 outputs x 128 rows x 16 vectors of 8 hidden units: 12 per thread
+  // 3 outputs x 128 rows x 16 vectors of 8 hidden units
+  constexpr int VPO = 128 * 16 / G::kThreads;              // vectors per thread and output
   const int64_t plane = (int64_t)p.heads * p.n_pad * m;   // elements per output
   __bf16 *dst = static_cast<__bf16 *>(p.out) + ((int64_t)h * p.n_pad + tok0) * m + u0;
 #pragma unroll
-  for (int it = 0; it < 12; ++it) {
-    const int k = it >> 2;
-    const int rem = t + 512 * (it & 3);
+  for (int it = 0; it < 3 * VPO; ++it) {
+    const int k = it / VPO;
+    const int rem = t + G::kThreads * (it % VPO);
     const int tr = rem >> 4, cu = rem & 15;
     const __bf16 *srcs = k == 0 ? o1 : (k == 1 ? o3 : oh);
     const bf16x8 v = *reinterpret_cast<const bf16x8 *>(srcs + st128(tr, 8 * cu));
@@ -554,7 +559,7 @@ int64_t big_pad_tokens(int64_t n) { return (n + 255) / 256 * 256; }
 
 hipError_t launch_big_fwd(const BigFwdParams &p, hipStream_t s) {
   const int64_t total = (int64_t)p.heads * (p.n_pad / FwdGeo::TM) * (p.m / FwdGeo::TN);
-  hipLaunchKernelGGL(big_fwd_kernel, dim3((unsigned)((total + 7) / 8 * 8)), dim3(512), 0, s, p);
+  hipLaunchKernelGGL(big_fwd_kernel, dim3((unsigned)((total + 7) / 8 * 8)), dim3(FwdGeo::kThreads), 0, s, p);
   return hipGetLastError();
 }
 
