@@ -26,18 +26,6 @@
 namespace ttt {
 namespace {
 
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N> __device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-// Workgroup barrier without the vmcnt(0) that __syncthreads adds (which would
-// also wait for the DMAs just issued for later stages).
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Launch-order block -> work item: blocks go round-robin over the 8 XCDs, so
 // item (b % 8) * per + b / 8 puts consecutive items (which share operand rows)
@@ -116,12 +104,12 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[NP][G::FM][G::FN], cons
   auto step = [&](int kc, const unsigned char *cur, unsigned char *refill) __attribute__((always_inline)) {
     const int later = nk - 1 - kc;        // chunks after kc already issued: min(later, NST - 2)
     if (G::NST > 3 && later >= 2)
-      wait_vm<2 * G::kPPW>();
+      wait_vmcnt<2 * G::kPPW>();
     else if (G::NST > 2 && later >= 1)
-      wait_vm<G::kPPW>();
+      wait_vmcnt<G::kPPW>();
     else
-      wait_vm<0>();
-    barrier_only();
+      wait_vmcnt<0>();
+    bare_barrier();
     if (kc + G::NST - 1 < nk) issue(kc + G::NST - 1, refill);
     compute(cur);
   };
@@ -379,10 +367,10 @@ __global__ __launch_bounds__(512) void big_contract_kernel(BigCtrParams p) {
   };
   auto step = [&](int blk, const unsigned char *cur, unsigned char *refill) __attribute__((always_inline)) {
     if (blk + 1 < nb)
-      wait_vm<L::kPPW>();
+      wait_vmcnt<L::kPPW>();
     else
-      wait_vm<0>();
-    barrier_only();
+      wait_vmcnt<0>();
+    bare_barrier();
     if (blk + 2 < nb) issue(blk + 2, refill);
     compute(cur);
   };

@@ -119,8 +119,36 @@ __device__ __forceinline__ void copy16_to_lds(const void *gsrc, unsigned char *l
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(gsrc),
                                    (__attribute__((address_space(3))) void *)(lds_wave_base), 16, 0, 0);
 }
+// buffer_load_dwordx4 ... lds: the same copy through a buffer view (wave-uniform base
+// and byte range in `rsrc`), each lane giving a 32-bit byte offset; fetches past the
+// range return zeros.  Keeps the per-lane address at one register instead of two.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset,
+                                              unsigned char *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(lds_wave_base), 16,
+                                           voffset, 0, 0, 0);
+}
+// Raw buffer view of `bytes` bytes at `base` (32-bit dword format word of gfx9).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
 // Wait for this wave's outstanding global/LDS operations (vmcnt = lgkmcnt = 0).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N> __device__ __forceinline__ void wait_vmcnt_lds() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+// Workgroup barrier without the vmcnt(0) that __syncthreads adds (which would
+// also wait for the DMAs just issued for later stages).
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bf16x8 cat8(const bf16x4 a, const bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

@@ -73,18 +73,6 @@ __device__ __forceinline__ float frag_sumsq(const f32x8 v) {
   return s;
 }
 
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-// Workgroup barrier without the vmcnt(0) that __syncthreads adds (which would
-// also wait for the DMAs just issued for later stages).
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <typename T>
 __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {

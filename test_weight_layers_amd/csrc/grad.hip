@@ -19,8 +19,6 @@
 // feeds dZ1, dZ3, H' straight back into the MFMA as operands: the tokens'
 // row order is permuted (perm_row) so that the accumulator layout of the first
 // product is the operand layout of the second, with no LDS round trip.
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -32,36 +30,49 @@ namespace {
 // (wave w and wave w + 4 run on one SIMD), so the hardware interleaves them:
 //   waves 0-3 ("forward"): z1, z3, p of a block for 16 hidden units each (MFMA,
 //     weights in registers, K/V fragments from LDS), then the SwiGLU backward (VALU);
-//     the packed bf16 operands dZ1, dZ3, H' go to LDS;
+//     the packed bf16 operands dZ1, dZ3, H' go to one of two LDS buffers;
 //   waves 4-7 ("contraction"): the token contractions of the previous block for
-//     the same hidden units, fp32 accumulators G1, G3, G2 in registers.
-// K and V of a block are DMA'd into LDS once (row-major, swizzled) into one of three
-// stages, with the block's rates; the forward waves read d-fragments as two 8-byte
-// halves, the contraction waves read the tile transposed (ds_read_b64_tr_b16).
-// Iteration i: forward of block i, contractions of block i-1, DMA of block i+1.
+//     the same hidden units, fp32 accumulators G1, G3, G2 in registers, and all of
+//     the staging DMA.
+// K and V of a block are DMA'd into LDS once (row-major, swizzled) into one of four
+// stages, with the block's rates; the forward waves read 16-byte d-fragments, the
+// contraction waves read the tile transposed (ds_read_b64_tr_b16).
+// Iteration i: DMA of block i+2, forward of block i, contractions of block i-1.  The
+// DMA has two iterations to land: the barrier that ends an iteration waits only for
+// the block needed next (s_waitcnt vmcnt(N) with the N copies just issued still in
+// flight), not for the one issued in it.
 template <int D>
 struct FastLayout {
   static constexpr int kChunks = D / 8;                   // 16-byte chunks per token row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTile = kTokBlock * kRowBytes;     // one K or V block
   static constexpr int kEta = 2 * kTile;                  // the block's 32 rates (fp32), 256 bytes reserved
-  static constexpr int kPk = kEta + 256;                  // packed dZ1, dZ3, H': [wave][3][lane] x 16 bytes
-  static constexpr int kStage = kPk + 4 * 3 * 64 * 16;
+  static constexpr int kStage = kEta + 256;
 };
+// packed dZ1, dZ3, H' of one block: [wave][3][lane] x 16 bytes
+constexpr int kPkBytes = 4 * 3 * 64 * 16;
 
 typedef unsigned long long u64;
 typedef u64 u64x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
+// contraction waves per hidden group (each takes D / kGradCS of the output columns)
+constexpr int kGradCS = 2;
+
+template <int D, int CS>
+__global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradParams p) {
   using L = FastLayout<D>;
   constexpr int KC = D / 32;   // reduction chunks over d
   constexpr int DT = D / 16;   // 16-wide d tiles of the outputs
-  // three separate arrays (not one indexed array), each named statically, so that
-  // the compiler can tell the stage being DMA'd from the ones being read
+  constexpr int DTW = DT / CS; // d tiles per contraction wave
+  constexpr int FR = CS == 1 ? 3 : 2;   // forward read ring (registers are scarcer at 3 waves per SIMD)
+  // separate arrays (not one indexed array), each named statically, so that the
+  // compiler can tell the stages apart
   __shared__ __attribute__((aligned(16))) unsigned char st0[L::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char st1[L::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char st2[L::kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[L::kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char pkb0[kPkBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char pkb1[kPkBytes];
 
   const int total = gridDim.x;
   const int b = blockIdx.x;
@@ -76,7 +87,9 @@ __global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
   // wave index, role and hidden group are wave-uniform: keep them scalar
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool forward_role = wv < 4;
-  const int w = wv & 3;
+  const int w = wv & 3;                 // hidden group (both roles)
+  const int c = wv - 4;                 // contraction wave index 0 .. 4 CS - 1
+  const int dh = c >> 2;                // its part of d: tiles dh DTW .. dh DTW + DTW - 1
   const int l = tid & 63, g = l >> 4, li = l & 15;
   const int hid0 = jt * kHidTile + 16 * w;
 
@@ -91,63 +104,79 @@ __global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
   // straight into LDS.  1 KB piece b of a stage holds matrix b / (NPIECE / 2) and
   // rows kRowsPer * (b % (NPIECE / 2)) ..; lane l fills row r = first + l / kChunks at
   // physical chunk p = l % kChunks, i.e. the logical chunk p ^ swizzle(r) of token
-  // row r.  Rows past n are fetched from row n-1; their rate is 0, which zeroes
-  // dH, dZ1, dZ3 and H' and so their whole contribution.
+  // row r.  Contraction wave 4 + c (c < NDMA) copies K pieces c * PPW .. and the V
+  // pieces of the same rows.  Rows past n are fetched from row n-1; their rate is 0,
+  // which zeroes dH, dZ1, dZ3 and H' and so their whole contribution.
+  // Only the contraction waves DMA: the compiler cannot tell a pending DMA into one
+  // stage from the forward waves' plain LDS reads of another, and would make those
+  // reads wait for it.
   constexpr int kRowsPer = 1024 / L::kRowBytes;           // token rows per 1 KB piece
   constexpr int NPIECE = 2 * L::kTile / 1024;             // K and V pieces per stage
-  constexpr int PPW = NPIECE / 8;                         // pieces per wave
+  constexpr int PPW = NPIECE / 2 >= 4 * CS ? NPIECE / 2 / (4 * CS) : 1;   // K pieces per DMA wave
+  constexpr int NDMA = NPIECE / 2 / PPW;                  // contraction waves that DMA
   const __bf16 *Kh = static_cast<const __bf16 *>(p.k) + (int64_t)h * D;
   const __bf16 *Vh = static_cast<const __bf16 *>(p.v) + (int64_t)h * D;
-  auto piece_row = [&](int q) { return kRowsPer * ((wv * PPW + q) % (NPIECE / 2)) + l / L::kChunks; };
-  unsigned soff[PPW];          // per-lane byte offset of each piece inside a block
   const unsigned row_bytes = (unsigned)(p.ld * 2);
-#pragma unroll
-  for (int q = 0; q < PPW; ++q) {
-    const int r = piece_row(q);
-    soff[q] = (unsigned)r * row_bytes + 16u * (unsigned)((l % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)));
-  }
-  // The rates of a block come with it (wave 0, one dword per lane) through a
+  // The rates of a block come with it (wave 4, one dword per lane) through a
   // range-checked buffer view that ends at token n: rates past n arrive as 0.
   const float *eta = p.eta + (int64_t)h * p.eta_hs;
   auto stage_block = [&](int blk, unsigned char *dst) {
+    if (forward_role || c >= NDMA) return;
     const int t0 = blk * kTokBlock;
-    if (wv == 0) {
+    if (wv == 4) {
       const int valid = n - t0 < kTokBlock ? n - t0 : kTokBlock;
-      const __amdgpu_buffer_rsrc_t er =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(eta + t0), (short)0, valid * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t er = buffer_view(eta + t0, 4u * (unsigned)valid);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void *)(dst + L::kEta), 4,
                                                4u * (unsigned)l, 0, 0, 0);
     }
-    // wave-uniform block bases; unsigned per-lane 32-bit offsets (a block spans 32 rows)
-    const char *kb = reinterpret_cast<const char *>(Kh + (int64_t)t0 * p.ld);
-    const char *vb = reinterpret_cast<const char *>(Vh + (int64_t)t0 * p.ld);
+    // Per-lane byte offset of each piece's rows inside a block, rebuilt here from the
+    // lane index (a few VALU operations) rather than held in registers across the
+    // loop: the empty asm keeps the compiler from hoisting them out of it.
+    int lane = l;
+    asm volatile("" : "+v"(lane));
+    auto piece_row = [&](int q) { return kRowsPer * (c * PPW + q) + lane / L::kChunks; };
+    unsigned soff[PPW];
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) {
+      const int r = piece_row(q);
+      soff[q] = (unsigned)r * row_bytes + 16u * (unsigned)((lane % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)));
+    }
+    // wave-uniform buffer views of the block's 32 rows; unsigned per-lane offsets
+    const __amdgpu_buffer_rsrc_t kr = buffer_view(Kh + (int64_t)t0 * p.ld, kTokBlock * row_bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_view(Vh + (int64_t)t0 * p.ld, kTokBlock * row_bytes);
     if (t0 + kTokBlock <= n) {                                    // wave-uniform: full block
 #pragma unroll
       for (int q = 0; q < PPW; ++q) {
-        const int piece = wv * PPW + q;
-        copy16_to_lds((piece >= NPIECE / 2 ? vb : kb) + soff[q], dst + piece * 1024);
+        const int piece = c * PPW + q;
+        copy16_to_lds(kr, soff[q], dst + piece * 1024);
+        copy16_to_lds(vr, soff[q], dst + (piece + NPIECE / 2) * 1024);
       }
     } else {                                                      // last block: clamp rows to n-1
 #pragma unroll
       for (int q = 0; q < PPW; ++q) {
-        const int piece = wv * PPW + q;
+        const int piece = c * PPW + q;
         const int r = piece_row(q), keep = n - 1 - t0;
         const unsigned off = r <= keep ? soff[q] : soff[q] - (unsigned)(r - keep) * row_bytes;
-        copy16_to_lds((piece >= NPIECE / 2 ? vb : kb) + off, dst + piece * 1024);
+        copy16_to_lds(kr, off, dst + piece * 1024);
+        copy16_to_lds(vr, off, dst + (piece + NPIECE / 2) * 1024);
       }
     }
   };
-  auto sync = [&]() {
-    wait_all_memory();
-    __syncthreads();
+  // End of an iteration: this wave's LDS writes and every DMA but the `inflight`
+  // copies it issued last are complete, then the workgroup barrier.
+  auto sync = [&](bool inflight) {
+    if (!inflight || forward_role || c >= NDMA) wait_vmcnt_lds<0>();
+    else if (wv == 4) wait_vmcnt_lds<2 * PPW + 1>();
+    else wait_vmcnt_lds<2 * PPW>();
+    bare_barrier();
   };
   // Pace keeping.  The m / 64 workgroups of one token range (one per hidden tile)
   // run on one XCD and read the same K/V blocks, which its L2 serves once while they
   // stay close; left alone they drift apart over thousands of blocks until the L2
-  // no longer holds a block between its readers.  Every kPace blocks, wave 0 counts
-  // the workgroup in at its group's counter and waits (bounded: the wait is only a
-  // hint, nothing depends on it) until every workgroup of the group has passed the
-  // previous checkpoint, so they stay within 2 kPace blocks of each other.
+  // no longer holds a block between its readers.  Every kPace iterations, wave 0
+  // counts the workgroup in at its group's counter and waits (bounded: the wait is
+  // only a hint, nothing depends on it) until every workgroup of the group has passed
+  // the previous checkpoint, so they stay within 2 kPace blocks of each other.
   constexpr int kPace = 32;
   unsigned *const pace = p.group_sync ? p.group_sync + split * p.heads + h : nullptr;
   auto keep_pace = [&](int i) {
@@ -162,75 +191,74 @@ __global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
       }
     }
   };
-  // this lane's 16-byte slot of operand op in the packed-operand area of a stage
-  const int pk_slot = L::kPk + ((w * 3) * 64 + l) * 16;
+  // this lane's 16-byte slot of operand op in a packed-operand buffer
+  const int pk_slot = ((w * 3) * 64 + l) * 16;
 
   if (nb > 0) {
     stage_block(blk0, st0);
-    sync();
+    if (nb > 1) stage_block(blk0 + 1, st1);
+    sync(nb > 1);
   }
-  // Both roles run iterations i = 0 .. nb with one barrier each: the forward waves
-  // idle in the last, the contraction waves in the first.  Block blk0 + i lives in
-  // stage i % 3; the loop is unrolled by 3 so that every stage is named statically.
+  // Both roles run iterations i = 0 .. nb with one barrier each.  Block blk0 + i
+  // lives in stage i % 4 and its packed operands in buffer i % 2; the loops are
+  // unrolled by 4 so that every stage is named statically.
+  const int iters = nb > 0 ? nb + 1 : 0;
   if (forward_role) {
-    // d-reduction fragments are read as two 8-byte halves; odd lane groups take the
-    // upper half first, which spreads one read over all 64 banks.  The MFMA only
-    // needs A and B to agree on the k order, so the weights use the same order.
-    const int hs = (g & 1) * 8;
     bf16x8 w1f[KC], w3f[KC], w2f[KC];   // B-operand fragments over d, this wave's 16 hidden units
     {
       const int64_t row = ((int64_t)h * p.m + hid0 + li) * D + 8 * g;
       const char *W1 = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.w1) + row);
       const char *W3 = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.w3) + row);
       const char *W2 = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.w2t) + row);
-      auto frag = [&](const char *src) {
-        const u64 lo = *reinterpret_cast<const u64 *>(src + hs), hi = *reinterpret_cast<const u64 *>(src + 8 - hs);
-        return __builtin_bit_cast(bf16x8, u64x2{lo, hi});
-      };
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        w1f[kc] = frag(W1 + 64 * kc);
-        w3f[kc] = frag(W3 + 64 * kc);
-        w2f[kc] = frag(W2 + 64 * kc);
+        w1f[kc] = *reinterpret_cast<const bf16x8 *>(W1 + 64 * kc);
+        w3f[kc] = *reinterpret_cast<const bf16x8 *>(W3 + 64 * kc);
+        w2f[kc] = *reinterpret_cast<const bf16x8 *>(W2 + 64 * kc);
       }
     }
     // LDS addresses.  Chunk 4kc + g of row rt with swizzle s: ((4kc + g) ^ s) * 16 =
-    // (16 (g ^ s)) ^ 64 kc, one XOR per read; rows perm_row(u, li).
-    int base_a[2][2];
+    // (16 (g ^ s)) ^ 64 kc, one XOR per read; rows perm_row(u, li).  A d-fragment is one
+    // 16-byte read: the 16 lanes of a ds_read_b128 phase (one g) hit 16 positions.
+    int base_a[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int rt = perm_row(u, li);
-      const int a = rt * L::kRowBytes + 16 * (g ^ (swz_rows(rt) & (L::kChunks - 1)));
-      base_a[u][0] = a + hs;
-      base_a[u][1] = a + 8 - hs;
+      base_a[u] = rt * L::kRowBytes + 16 * (g ^ (swz_rows(rt) & (L::kChunks - 1)));
     }
-    // forward + backward of the block in stage `cur`; packed operands into `cur`
-    auto forward_block = [&](unsigned char *cur) {
+    // Products of the block in `cur`, its SwiGLU backward, and the packed operands
+    // into `pkw`.  Each reduction chunk ends in a scheduling barrier, so that the
+    // reads for chunk kc + FR - 1 issue before the products of chunk kc.
+    auto forward_block = [&](const unsigned char *cur, unsigned char *pkw) {
       f32x4 z1[2], z3[2], pp[2];
-      bf16x8 kf[2], vf[2];
-      auto lda = [&](int i, int slot) {
-        const int u = i / KC, kc = i % KC;
-        // V's addresses pass through an empty asm: otherwise the K and V halves
-        // (16 KB apart) merge into paired reads whose results need register moves
-        int v0 = base_a[u][0] ^ (64 * kc), v1 = base_a[u][1] ^ (64 * kc);
-        const unsigned char *p0 = cur + v0, *p1 = cur + v1;
-        asm volatile("" : "+v"(v0), "+v"(v1));
-        const unsigned char *q0 = cur + L::kTile + v0, *q1 = cur + L::kTile + v1;
-        kf[slot] = __builtin_bit_cast(bf16x8, u64x2{*reinterpret_cast<const u64 *>(p0),
-                                                    *reinterpret_cast<const u64 *>(p1)});
-        vf[slot] = __builtin_bit_cast(bf16x8, u64x2{*reinterpret_cast<const u64 *>(q0),
-                                                    *reinterpret_cast<const u64 *>(q1)});
-      };
-      constexpr int NA = 2 * KC;
-      lda(0, 0);
+      bf16x8 kf[FR][2], vf[FR][2];
+      auto lda = [&](int kc, int slot) {
 #pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const int u = i / KC, kc = i % KC;
-        if (kc == 0) z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
-        if (i + 1 < NA) lda(i + 1, (i + 1) & 1);
-        z1[u] = mma(kf[i & 1], w1f[kc], z1[u]);
-        z3[u] = mma(kf[i & 1], w3f[kc], z3[u]);
-        pp[u] = mma(vf[i & 1], w2f[kc], pp[u]);
+        for (int u = 0; u < 2; ++u) {
+          // V's address passes through an empty asm: otherwise the K and V reads
+          // (16 KB apart) merge into paired reads whose results need register moves
+          int v0 = base_a[u] ^ (64 * kc);
+          const unsigned char *p0 = cur + v0;
+          asm volatile("" : "+v"(v0));
+          kf[slot][u] = *reinterpret_cast<const bf16x8 *>(p0);
+          vf[slot][u] = *reinterpret_cast<const bf16x8 *>(cur + L::kTile + v0);
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < 2; ++u) z1[u] = z3[u] = pp[u] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < FR - 1 && j < KC; ++j) lda(j, j);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (kc + FR - 1 < KC) lda(kc + FR - 1, (kc + FR - 1) % FR);
+        const int s = kc % FR;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          z1[u] = mma(kf[s][u], w1f[kc], z1[u]);
+          z3[u] = mma(kf[s][u], w3f[kc], z3[u]);
+          pp[u] = mma(vf[s][u], w2f[kc], pp[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // rates of this lane's tokens 8g .. 8g+7
       const f32x4 ea = *reinterpret_cast<const f32x4 *>(cur + L::kEta + 32 * g);
@@ -250,29 +278,30 @@ __global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
         pk1[v] = (__bf16)(dh * y * (sg + act - act * sg));
         pkh[v] = (__bf16)(ne * (act * y));
       }
-      *reinterpret_cast<bf16x8 *>(cur + pk_slot) = pk1;
-      *reinterpret_cast<bf16x8 *>(cur + pk_slot + 1024) = pk3;
-      *reinterpret_cast<bf16x8 *>(cur + pk_slot + 2048) = pkh;
+      *reinterpret_cast<bf16x8 *>(pkw + pk_slot) = pk1;
+      *reinterpret_cast<bf16x8 *>(pkw + pk_slot + 1024) = pk3;
+      *reinterpret_cast<bf16x8 *>(pkw + pk_slot + 2048) = pkh;
     };
-    auto step = [&](int i, unsigned char *cur, unsigned char *next) {
-      if (i + 1 < nb) stage_block(blk0 + i + 1, next);
-      forward_block(cur);
+    // iteration i: forward of block i (stage i % 4, packed operands to buffer i % 2)
+    auto step = [&](int i, const unsigned char *cur, unsigned char *pkw) {
+      if (i < nb) forward_block(cur, pkw);
       keep_pace(i);
-      sync();
+      sync(false);
     };
     int i = 0;
-    for (; i + 3 <= nb; i += 3) {
-      step(i, st0, st1);
-      step(i + 1, st1, st2);
-      step(i + 2, st2, st0);
+    for (; i + 4 <= iters; i += 4) {
+      step(i, st0, pkb0);
+      step(i + 1, st1, pkb1);
+      step(i + 2, st2, pkb0);
+      step(i + 3, st3, pkb1);
     }
-    if (i < nb) step(i, st0, st1);
-    if (i + 1 < nb) step(i + 1, st1, st2);
-    if (nb > 0) sync();                // iteration nb: the contraction of the last block
+    if (i < iters) step(i, st0, pkb0);
+    if (i + 1 < iters) step(i + 1, st1, pkb1);
+    if (i + 2 < iters) step(i + 2, st2, pkb0);
   } else {
-    f32x4 a1[DT], a3[DT], a2[DT];
+    f32x4 a1[DTW], a3[DTW], a2[DTW];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) a1[t] = a3[t] = a2[t] = f32x4{0, 0, 0, 0};
+    for (int t = 0; t < DTW; ++t) a1[t] = a3[t] = a2[t] = f32x4{0, 0, 0, 0};
     // transposed reads: lane (g, li) supplies row 8g + 4q + li/4, column 16 dt + 4 (li % 4)
     // and receives rows 8g + 4q .. +3 of column 16 dt + li; chunk 2dt + e of row r with
     // swizzle s: ((2dt + e) ^ s) * 16 = (16 (e ^ s)) ^ 32 dt
@@ -281,65 +310,81 @@ __global__ __launch_bounds__(512, 1) void grad_fast_kernel(GradParams p) {
     for (int q = 0; q < 2; ++q) {
       const int row = 8 * g + 4 * q + (li >> 2);
       const int e = (li & 3) >> 1;
-      base_b[q] = row * L::kRowBytes + 16 * (e ^ (swz_rows(row) & (L::kChunks - 1))) + 8 * (li & 1);
+      // tile dt0 + j of this wave: 32 (dt0 + j) = 32 dt0 ^ 32 j (dt0 is a multiple of DTW > j)
+      base_b[q] = (row * L::kRowBytes + 16 * (e ^ (swz_rows(row) & (L::kChunks - 1))) + 8 * (li & 1)) ^ (32 * DTW * dh);
     }
-    // G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H' for the block in stage `prev`
-    auto contract_block = [&](const unsigned char *prev) {
-      const bf16x8 pk1 = *reinterpret_cast<const bf16x8 *>(prev + pk_slot);
-      const bf16x8 pk3 = *reinterpret_cast<const bf16x8 *>(prev + pk_slot + 1024);
-      const bf16x8 pkh = *reinterpret_cast<const bf16x8 *>(prev + pk_slot + 2048);
+    // G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H' for the block in stage `blk` with its
+    // packed operands pk1, pk3, pkh; the transposed reads run one 16-column tile ahead
+    // (scheduling barrier per tile)
+    auto contract_block = [&](const unsigned char *blk, const bf16x8 pk1, const bf16x8 pk3, const bf16x8 pkh) {
       bf16x8 ktf[2], vtf[2];
       auto ldb = [&](int dt, int slot) {
         // the bases pass through an empty asm so that each address is formed (one
         // XOR) right before its read instead of 32 of them being held in registers
         int b0 = base_b[0], b1 = base_b[1];
         asm volatile("" : "+v"(b0), "+v"(b1));
-        const unsigned char *p0 = prev + (b0 ^ (32 * dt));
-        const unsigned char *p1 = prev + (b1 ^ (32 * dt));
+        const unsigned char *p0 = blk + (b0 ^ (32 * dt));
+        const unsigned char *p1 = blk + (b1 ^ (32 * dt));
         ktf[slot] = cat8(lds_read_tr16(p0), lds_read_tr16(p1));
         vtf[slot] = cat8(lds_read_tr16(p0 + L::kTile), lds_read_tr16(p1 + L::kTile));
       };
       ldb(0, 0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        if (dt + 1 < DT) ldb(dt + 1, (dt + 1) & 1);
-        a1[dt] = mma(pk1, ktf[dt & 1], a1[dt]);
-        a3[dt] = mma(pk3, ktf[dt & 1], a3[dt]);
-        a2[dt] = mma(vtf[dt & 1], pkh, a2[dt]);
+      for (int dt = 0; dt < DTW; ++dt) {
+        if (dt + 1 < DTW) ldb(dt + 1, (dt + 1) & 1);
+        const int s = dt & 1;
+        a1[dt] = mma(pk1, ktf[s], a1[dt]);
+        a3[dt] = mma(pk3, ktf[s], a3[dt]);
+        a2[dt] = mma(vtf[s], pkh, a2[dt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    auto step = [&](int i, const unsigned char *prev, unsigned char *next) {
-      if (i + 1 < nb) stage_block(blk0 + i + 1, next);
-      if (i > 0) contract_block(prev);
-      sync();
+    // iteration i: DMA of block i + 2 (stage (i + 2) % 4), contraction of block i - 1
+    // (stage (i - 1) % 4, packed operands in buffer (i - 1) % 2).  Iteration 0 has no
+    // contraction and runs before the loop, which then starts at i = 1.
+    // The packed operands are read before the DMA is issued: plain LDS reads after it
+    // would make the compiler wait for the DMA first.
+    auto step = [&](int i, const unsigned char *ctr, unsigned char *dma, const unsigned char *pkr) {
+      const bool issue = i + 2 < nb;
+      const bf16x8 pk1 = *reinterpret_cast<const bf16x8 *>(pkr + pk_slot);
+      const bf16x8 pk3 = *reinterpret_cast<const bf16x8 *>(pkr + pk_slot + 1024);
+      const bf16x8 pkh = *reinterpret_cast<const bf16x8 *>(pkr + pk_slot + 2048);
+      if (issue) stage_block(blk0 + i + 2, dma);
+      // always true here; written as a test because the unconditional form makes
+      // the register allocator spill accumulators at d = 256
+      if (i <= nb) contract_block(ctr, pk1, pk3, pkh);
+      sync(issue);
     };
-    // iteration i: contraction of block i - 1 (stage (i - 1) % 3), DMA of block i + 1
-    int i = 0;
-    for (; i + 3 <= nb; i += 3) {
-      step(i, st2, st1);
-      step(i + 1, st0, st2);
-      step(i + 2, st1, st0);
+    if (iters > 0) {
+      const bool issue = nb > 2;
+      if (issue) stage_block(blk0 + 2, st2);
+      sync(issue);
     }
-    if (i < nb) step(i, st2, st1);
-    if (i + 1 < nb) step(i + 1, st0, st2);
-    if (nb > 0) {                      // iteration nb: the last block, stage (nb - 1) % 3
-      const int last = (nb - 1) % 3;
-      contract_block(last == 0 ? st0 : (last == 1 ? st1 : st2));
-      sync();
+    int i = 1;
+    for (; i + 4 <= iters; i += 4) {
+      step(i, st0, st3, pkb0);
+      step(i + 1, st1, st0, pkb1);
+      step(i + 2, st2, st1, pkb0);
+      step(i + 3, st3, st2, pkb1);
     }
+    if (i < iters) step(i, st0, st3, pkb0);
+    if (i + 1 < iters) step(i + 1, st1, st0, pkb1);
+    if (i + 2 < iters) step(i + 2, st2, st1, pkb0);
 
     // partials: G1/G3 rows hid0 + 4g + r, cols 16 dt + li;  G2 rows 16 dt + 4g + r, cols hid0 + li
     const int64_t mat = (int64_t)p.m * D;
     float *P1 = p.part + ((int64_t)split * 3 * p.heads + h) * mat;
     float *P3 = P1 + p.heads * mat;
     float *P2 = P3 + p.heads * mat;
+    const int dt0 = DTW * dh;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int j = 0; j < DTW; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        P1[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a1[dt][r];
-        P3[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a3[dt][r];
-        P2[(int64_t)(16 * dt + 4 * g + r) * p.m + hid0 + li] = a2[dt][r];
+        const int dt = dt0 + j;
+        P1[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a1[j][r];
+        P3[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a3[j][r];
+        P2[(int64_t)(16 * dt + 4 * g + r) * p.m + hid0 + li] = a2[j][r];
       }
   }
 }
@@ -501,9 +546,9 @@ hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int gri
   if (fast) {
     switch (d) {
       // 8 waves: 4 forward + 4 contraction (see grad_fast_kernel)
-      case 64: hipLaunchKernelGGL(grad_fast_kernel<64>, dim3(grid), dim3(512), 0, s, p); break;
-      case 128: hipLaunchKernelGGL(grad_fast_kernel<128>, dim3(grid), dim3(512), 0, s, p); break;
-      case 256: hipLaunchKernelGGL(grad_fast_kernel<256>, dim3(grid), dim3(512), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((grad_fast_kernel<64, kGradCS>), dim3(grid), dim3((4 + 4 * kGradCS) * 64), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((grad_fast_kernel<128, kGradCS>), dim3(grid), dim3((4 + 4 * kGradCS) * 64), 0, s, p); break;
+      case 256: hipLaunchKernelGGL((grad_fast_kernel<256, kGradCS>), dim3(grid), dim3((4 + 4 * kGradCS) * 64), 0, s, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
