@@ -46,20 +46,29 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace collapsed (string literals in
+    these files hold no comment markers), so that editing a comment keeps the digest."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def grad_source_digest():
-    """sha256 over what the gradient kernel is compiled from: grad.hip, common.h and
+    """sha256 over the code the gradient kernel is compiled from: grad.hip, common.h and
     the part of kernels.h up to the end of GradParams (tile constants and the
     parameter block); declarations after it belong to other kernels."""
     import hashlib
     csrc = os.path.join(ROOT, "test_weight_layers_amd", "csrc")
     h = hashlib.sha256()
     for f in ("grad.hip", "common.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
-    with open(os.path.join(csrc, "kernels.h"), "rb") as fh:
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(_code_only(fh.read()).encode())
+    with open(os.path.join(csrc, "kernels.h")) as fh:
         text = fh.read()
-    start = text.index(b"struct GradParams")
-    h.update(text[:text.index(b"};", start) + 2])
+    start = text.index("struct GradParams")
+    h.update(_code_only(text[:text.index("};", start) + 2]).encode())
     return h.hexdigest()
 
 
@@ -71,7 +80,7 @@ def measured_traffic(d):
         return None
     rec = {}
     for line in open(path):
-        if line.startswith("traffic_bytes_per_launch grad_fast_kernel<256>:"):
+        if line.startswith("traffic_bytes_per_launch grad_fast_kernel<256"):
             rec["bytes"] = float(line.split(":")[1])
         elif line.startswith("gradient_kernel_source_sha256:"):
             rec["sha"] = line.split(":")[1].strip()

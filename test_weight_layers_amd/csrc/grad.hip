@@ -26,14 +26,15 @@ namespace ttt {
 namespace {
 
 // ---------------------------------------------------------------- fast path
-// bf16 tokens, D <= 256.  A workgroup has 8 waves in two roles that share the SIMDs
-// (wave w and wave w + 4 run on one SIMD), so the hardware interleaves them:
+// bf16 tokens, D <= 256.  A workgroup has 4 + 4 CS waves in two roles that share the
+// SIMDs (waves w, w + 4, w + 8 run on one SIMD), so the hardware interleaves them:
 //   waves 0-3 ("forward"): z1, z3, p of a block for 16 hidden units each (MFMA,
 //     weights in registers, K/V fragments from LDS), then the SwiGLU backward (VALU);
 //     the packed bf16 operands dZ1, dZ3, H' go to one of two LDS buffers;
-//   waves 4-7 ("contraction"): the token contractions of the previous block for
-//     the same hidden units, fp32 accumulators G1, G3, G2 in registers, and all of
-//     the staging DMA.
+//   waves 4 .. 3 + 4 CS ("contraction"): the token contractions of the previous block
+//     for the same hidden units, CS waves per hidden group, each with D / CS of the
+//     output columns and their fp32 accumulators G1, G3, G2 in registers; these
+//     waves also issue all of the staging DMA.
 // K and V of a block are DMA'd into LDS once (row-major, swizzled) into one of four
 // stages, with the block's rates; the forward waves read 16-byte d-fragments, the
 // contraction waves read the tile transposed (ds_read_b64_tr_b16).
@@ -545,7 +546,7 @@ int grad_general_dc(int d, bool bf16) {
 hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int grid, hipStream_t s) {
   if (fast) {
     switch (d) {
-      // 8 waves: 4 forward + 4 contraction (see grad_fast_kernel)
+      // 4 forward + 4 kGradCS contraction waves (see grad_fast_kernel)
       case 64: hipLaunchKernelGGL((grad_fast_kernel<64, kGradCS>), dim3(grid), dim3((4 + 4 * kGradCS) * 64), 0, s, p); break;
       case 128: hipLaunchKernelGGL((grad_fast_kernel<128, kGradCS>), dim3(grid), dim3((4 + 4 * kGradCS) * 64), 0, s, p); break;
       case 256: hipLaunchKernelGGL((grad_fast_kernel<256, kGradCS>), dim3(grid), dim3((4 + 4 * kGradCS) * 64), 0, s, p); break;
