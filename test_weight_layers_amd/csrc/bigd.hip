@@ -147,12 +147,31 @@ __global__ __launch_bounds__(FwdGeo::kThreads) void big_fwd_kernel(BigFwdParams 
   const int tiles_u = p.m / G::TN;
   const int64_t tiles_t = p.n_pad / G::TM;
   const int64_t total = (int64_t)p.heads * tiles_t * tiles_u;
-  const int64_t item = xcd_work_item(total);
-  if (item >= total) return;
-  const int tu = (int)(item % tiles_u);
-  const int64_t ht = item / tiles_u;
-  const int64_t tt = ht % tiles_t;
-  const int h = (int)(ht / tiles_t);
+  // Work order.  A tile reads 128 K/V token rows and 3 x 128 weight rows over all of d.
+  // When the hidden tiles split evenly over the 8 XCDs, XCD x keeps hidden tiles
+  // x * tiles_u / 8 .. for every token tile (their weights, 1.5 MB at d = 1024 and
+  // m = 2048, stay in its L2) and runs them token tile by token tile, so the tiles in
+  // flight together share K/V rows too.  Otherwise each XCD cycles through all hidden
+  // tiles of a token tile, and the weights stream from beyond L2.
+  int tu;
+  int64_t tt;
+  int h;
+  if (tiles_u % 8 == 0) {
+    const int per_x = tiles_u / 8;
+    const int64_t j = blockIdx.x >> 3;   // launch-order position within XCD blockIdx.x % 8
+    if (j >= total / 8) return;
+    tu = (int)(blockIdx.x & 7) * per_x + (int)(j % per_x);
+    const int64_t ht = j / per_x;
+    tt = ht % tiles_t;
+    h = (int)(ht / tiles_t);
+  } else {
+    const int64_t item = xcd_work_item(total);
+    if (item >= total) return;
+    tu = (int)(item % tiles_u);
+    const int64_t ht = item / tiles_u;
+    tt = ht % tiles_t;
+    h = (int)(ht / tiles_t);
+  }
   const int64_t tok0 = tt * G::TM;
   const int u0 = tu * G::TN;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 4, li = l & 15;
