@@ -87,7 +87,8 @@ def test_zipmap_single_head_1024_2048():
 
 
 @pytest.mark.parametrize("general", [False, True])
-@pytest.mark.parametrize("shape", [(2, 512, 512, 1000, 77), (2, 768, 256, 333, 5), (1, 1024, 512, 70, 300)])
+@pytest.mark.parametrize("shape", [(2, 512, 512, 1000, 77), (2, 768, 256, 333, 5), (1, 1024, 512, 70, 300),
+                                   (1, 512, 1024, 333, 7)])
 def test_wide_heads(shape, general):
     # the two-kernel wide-head path (d >= 512) and the general kernels, both against
     # the oracle: ragged token tails, fewer tokens than one 256-row tile, Nq > N
@@ -98,6 +99,13 @@ def test_wide_heads(shape, general):
 def test_two_inner_steps_with_conv():
     cfg = cfg_like("c3", frames=2)
     _check(cfg, steps=2)
+
+
+@pytest.mark.parametrize("n,splits", [(1, 0), (31, 0), (33, 0), (64, 1), (95, 2), (2000, 60)])
+def test_fast_gradient_few_blocks_per_split(n, splits):
+    # The fast gradient kernel stages K/V two 32-token blocks ahead; splits of one or
+    # two blocks (and splits with none, when n is tiny) take its short pipeline paths.
+    _check(cfg_like("c4", heads=2), n=n, nq_extra=3, splits=splits)
 
 
 def test_many_splits_and_single_split_agree():
