@@ -1,7 +1,7 @@
 """GPU parity at the workloads' full sizes, in the configuration bench.py times.
 
 The fp32 CPU oracle runs the whole layer at full size (about a minute on the
-GPU machine's host cores for the 1000-frame workload); every output is compared,
+host's CPU cores for the 1000-frame workload); every output is compared,
 per head and per matrix, against the bf16 gate of 2e-2.  The oracle's fp32
 rounding is 1e-5-level (pinned against fp64 in test_oracle.py), far inside it.
 The streaming workload is checked on its first chunks against the oracle's
