@@ -275,7 +275,8 @@ __device__ __forceinline__ void tile_nt(const float *__restrict__ P, int ldp, co
 // tile_nt with each fp32 operand split into bf16 hi + lo (x = hi + lo to about 16
 // significant bits) and the product taken as hi*hi + hi*lo + lo*hi on bf16 MFMA,
 // fp32 accumulation: about 2e-5 relative error on Newton-Schulz's output (fp32
-// products give 2e-6) for a fifth of the fp32-MFMA cycles.
+// products give 2e-6) for a fifth of the fp32-MFMA cycles.  The global loads run
+// two K chunks ahead (two register sets, one per LDS buffer).
 __device__ __forceinline__ void split4(const f32x4 v, __bf16 *hi, __bf16 *lo) {
   bf16x4 h, l;
 #pragma unroll
@@ -292,39 +293,36 @@ __device__ __forceinline__ void tile_nt_split(const float *__restrict__ P, int l
   const int lr = t >> 4, lc = (t & 15) * 4;
 #pragma unroll
   for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x4{0, 0, 0, 0};
-  f32x4 pa[4], pb[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 16 * u) * ldp + lc);
-    pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 16 * u) * ldq + lc);
-  }
-  const int nk = K / kKc;
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
+  f32x4 pa[2][4], pb[2][4];
+  auto load = [&](int kc, int s) {
+    const int k0 = kc * kKc;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      split4(pa[u], &sm.h.ah[buf][lr + 16 * u][lc], &sm.h.al[buf][lr + 16 * u][lc]);
-      split4(pb[u], &sm.h.bh[buf][lr + 16 * u][lc], &sm.h.bl[buf][lr + 16 * u][lc]);
+      pa[s][u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 16 * u) * ldp + k0 + lc);
+      pb[s][u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 16 * u) * ldq + k0 + lc);
+    }
+  };
+  const int nk = K / kKc;
+  load(0, 0);
+  if (nk > 1) load(1, 1);
+  auto chunk = [&](int kc, int s) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      split4(pa[s][u], &sm.h.ah[s][lr + 16 * u][lc], &sm.h.al[s][lr + 16 * u][lc]);
+      split4(pb[s][u], &sm.h.bh[s][lr + 16 * u][lc], &sm.h.bl[s][lr + 16 * u][lc]);
     }
     __syncthreads();
-    if (kc + 1 < nk) {
-      const int k0 = (kc + 1) * kKc;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        pa[u] = *reinterpret_cast<const f32x4 *>(P + (int64_t)(lr + 16 * u) * ldp + k0 + lc);
-        pb[u] = *reinterpret_cast<const f32x4 *>(Q + (int64_t)(lr + 16 * u) * ldq + k0 + lc);
-      }
-    }
+    if (kc + 2 < nk) load(kc + 2, s);
     const int ra = (w >> 1) * 32 + li, rb = (w & 1) * 32 + li;
 #pragma unroll
     for (int kk = 0; kk < kKc; kk += 32) {
       bf16x8 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        ah[i] = ld8(&sm.h.ah[buf][ra + 16 * i][kk + 8 * g]);
-        al[i] = ld8(&sm.h.al[buf][ra + 16 * i][kk + 8 * g]);
-        bh[i] = ld8(&sm.h.bh[buf][rb + 16 * i][kk + 8 * g]);
-        bl[i] = ld8(&sm.h.bl[buf][rb + 16 * i][kk + 8 * g]);
+        ah[i] = ld8(&sm.h.ah[s][ra + 16 * i][kk + 8 * g]);
+        al[i] = ld8(&sm.h.al[s][ra + 16 * i][kk + 8 * g]);
+        bh[i] = ld8(&sm.h.bh[s][rb + 16 * i][kk + 8 * g]);
+        bl[i] = ld8(&sm.h.bl[s][rb + 16 * i][kk + 8 * g]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -335,7 +333,13 @@ __device__ __forceinline__ void tile_nt_split(const float *__restrict__ P, int l
           acc[i][j] = mma(ah[i], bh[j], acc[i][j]);
         }
     }
+  };
+  int kc = 0;
+  for (; kc + 2 <= nk; kc += 2) {
+    chunk(kc, 0);
+    chunk(kc + 1, 1);
   }
+  if (kc < nk) chunk(kc, 0);
 }
 
 // Deterministic block sum (every workgroup computes the same value the same way).
