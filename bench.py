@@ -158,7 +158,10 @@ def cpu_baseline(cfg, frames):
 
 def linear_sweep(steps, warmup):
     """Update (1 step) + apply on the same N tokens of the ZipMap 4x256/512 shape at
-    125..2000 frames (prefixes of one draw); least-squares fit of time against N."""
+    125..2000 frames (prefixes of one draw); least-squares fit of time against N.
+    Beside it, the apply of one fixed batch of queries (32 frames) with the weights
+    each N produced: a query's cost does not depend on how many tokens were absorbed
+    (ZipMap 关键设计 4, querying the fast weights as a scene state)."""
     import numpy as np
     import torch
     from dataclasses import replace
@@ -171,7 +174,11 @@ def linear_sweep(steps, warmup):
     full = synth.to_device(synth.make_inputs(cfg), "cuda")
     H, d, m = cfg.heads, cfg.d, cfg.m
     w0 = (full.w1, full.w3, full.w2)
-    rows = []
+    nfix = 32 * cfg.tokens_per_frame
+    q_fix = full.q[:nfix]
+    o_fix = torch.empty((nfix, H * d), dtype=q_fix.dtype, device="cuda")
+    ws_f = torch.empty(ttt.apply_workspace_bytes(H, d, m, nfix, q_fix.dtype), dtype=torch.uint8, device="cuda")
+    rows, fixed = [], []
     for f in frames:
         n = f * cfg.tokens_per_frame
         k, v, q, eta = full.k[:n], full.v[:n], full.q[:n], full.eta[:, :n]
@@ -192,7 +199,16 @@ def linear_sweep(steps, warmup):
             step()
         torch.cuda.synchronize()
         rows.append((n, (time.perf_counter() - t0) / steps))
-        print(json.dumps({"sweep_frames": f, "tokens": n, "ms": rows[-1][1] * 1e3}), flush=True)
+        for _ in range(warmup):
+            ttt.apply(w_out, q_fix, out=o_fix, workspace=ws_f)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ttt.apply(w_out, q_fix, out=o_fix, workspace=ws_f)
+        torch.cuda.synchronize()
+        fixed.append((time.perf_counter() - t0) / steps)
+        print(json.dumps({"sweep_frames": f, "tokens": n, "ms": rows[-1][1] * 1e3,
+                          "apply_fixed_ms": fixed[-1] * 1e3}), flush=True)
     ns = np.array([r[0] for r in rows], float)
     ts = np.array([r[1] for r in rows], float)
     A = np.stack([np.ones_like(ns), ns], 1)
@@ -204,7 +220,9 @@ def linear_sweep(steps, warmup):
            "frames": frames, "tokens": ns.tolist(), "seconds": ts.tolist(), "t0_s": t0,
            "beta_s_per_token": beta, "r2": r2, "max_rel_residual": float(np.max(np.abs(ts - fit) / ts)),
            "t0_over_t_at_1000_frames": float(t0 / ts[i1000]),
-           "tokens_per_s_asymptotic": 1.0 / beta}
+           "tokens_per_s_asymptotic": 1.0 / beta,
+           "apply_fixed_queries": nfix, "apply_fixed_seconds": fixed,
+           "apply_fixed_spread": float(max(fixed) / min(fixed) - 1.0)}
     print(json.dumps(out), flush=True)
 
 
