@@ -139,7 +139,7 @@ hipError_t launch_gate(const GateParams &p, bool bf16, hipStream_t s);
 // Wide heads (bf16, d in {512, 768, 1024}, m % 256 == 0): the update and apply
 // split at the hidden layer into dense contractions (bigd.hip).
 bool big_supported(int d, int m, bool bf16);
-int64_t big_pad_tokens(int64_t n);          // token rows of the intermediates (multiple of 256)
+int64_t big_pad_tokens(int64_t n);          // token rows of the intermediates (multiple of 768)
 int big_contract_tiles(int d, int m, int mode);
 struct BigFwdParams {                       // dZ1, dZ3, H' = SwiGLU backward of K, V against W
   const void *k, *v;                        // [n][ld] bf16 token rows
