@@ -97,6 +97,13 @@ __device__ __forceinline__ int swz_rows(int r) {
 // perm_row(u, 0..15) at one chunk: row bits (0, 1, 3, 4) onto position bits
 // (0, 1, 2, 3) measured conflict-free on gfx950 (swz_rows is not for this pattern).
 __device__ __forceinline__ int swz_rows_b128(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
+// Row-major tile with 512-byte rows read both ways: ds_read_b128 by 16 lanes on rows
+// perm_row(u, 0..15) at one chunk, and ds_read_b64_tr_b16 as described for swz_rows.
+// The first pattern is conflict-free only when position bit 0 follows row bit 0 or 1,
+// the second only when it follows row bit 4, for every one-to-one map; measured on
+// gfx950, both are conflict-free when row bit 4 is left out and position bits
+// (0, 1, 2, 3) follow row bits (0, 0, 1, 3).
+__device__ __forceinline__ int swz_kv(int r) { return 3 * (r & 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3); }
 // Tile with 64-byte rows (4 chunks, 4 rows per 256 bytes): chunk a of row r lives at
 // a ^ swz_64(r), a bijection on row bits (2, 3) within each r % 4 class, so 16 lanes
 // reading rows R..R+15 (R % 16 == 0) at one chunk hit 16 positions.

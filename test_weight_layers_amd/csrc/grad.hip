@@ -140,7 +140,7 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
 #pragma unroll
     for (int q = 0; q < PPW; ++q) {
       const int r = piece_row(q);
-      soff[q] = (unsigned)r * row_bytes + 16u * (unsigned)((lane % L::kChunks) ^ (swz_rows(r) & (L::kChunks - 1)));
+      soff[q] = (unsigned)r * row_bytes + 16u * (unsigned)((lane % L::kChunks) ^ (swz_kv(r) & (L::kChunks - 1)));
     }
     // wave-uniform buffer views of the block's 32 rows; unsigned per-lane offsets
     const __amdgpu_buffer_rsrc_t kr = buffer_view(Kh + (int64_t)t0 * p.ld, kTokBlock * row_bytes);
@@ -220,12 +220,12 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     }
     // LDS addresses.  Chunk 4kc + g of row rt with swizzle s: ((4kc + g) ^ s) * 16 =
     // (16 (g ^ s)) ^ 64 kc, one XOR per read; rows perm_row(u, li).  A d-fragment is one
-    // 16-byte read: the 16 lanes of a ds_read_b128 phase (one g) hit 16 positions.
+    // 16-byte read, conflict-free under swz_kv (as are the contraction waves' reads).
     int base_a[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int rt = perm_row(u, li);
-      base_a[u] = rt * L::kRowBytes + 16 * (g ^ (swz_rows(rt) & (L::kChunks - 1)));
+      base_a[u] = rt * L::kRowBytes + 16 * (g ^ (swz_kv(rt) & (L::kChunks - 1)));
     }
     // Products of the block in `cur`, its SwiGLU backward, and the packed operands
     // into `pkw`.  Each reduction chunk ends in a scheduling barrier, so that the
@@ -312,7 +312,7 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
       const int row = 8 * g + 4 * q + (li >> 2);
       const int e = (li & 3) >> 1;
       // tile dt0 + j of this wave: 32 (dt0 + j) = 32 dt0 ^ 32 j (dt0 is a multiple of DTW > j)
-      base_b[q] = (row * L::kRowBytes + 16 * (e ^ (swz_rows(row) & (L::kChunks - 1))) + 8 * (li & 1)) ^ (32 * DTW * dh);
+      base_b[q] = (row * L::kRowBytes + 16 * (e ^ (swz_kv(row) & (L::kChunks - 1))) + 8 * (li & 1)) ^ (32 * DTW * dh);
     }
     // G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H' for the block in stage `blk` with its
     // packed operands pk1, pk3, pkh; the transposed reads run one 16-column tile ahead
