@@ -54,8 +54,9 @@ struct NtGeo {
   static_assert(WM % 16 == 0 && WN % 16 == 0, "tile shape");
 };
 
-// 16-byte piece c (0..3) of staged 64-byte row r sits at c ^ swz_64(r): 16 lanes
-// reading rows R..R+15 (R % 16 == 0) at one piece hit 16 distinct positions.
+// 16-byte piece c (0..3) of staged 64-byte row r sits at c ^ swz_64(r), under which
+// the fragment reads (rows R..R+15, R % 16 == 0, lane group g at piece g) are
+// conflict-free.
 __device__ __forceinline__ bf16x8 nt_frag(const unsigned char *stage, int r, int g) {
   return *reinterpret_cast<const bf16x8 *>(stage + r * 64 + ((g ^ swz_64(r)) << 4));
 }
