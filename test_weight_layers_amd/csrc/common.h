@@ -84,12 +84,13 @@ __device__ __forceinline__ int perm_row(int u, int i) { return 8 * (i >> 2) + 4 
 //
 // Row-major tile with rows of >= 256 bytes: chunk c of row r lives at c ^ swz_rows(r).
 // swz_rows maps row bits (0, 1, 3, 4) one-to-one onto position bits (1, 2, 3, 0), so
-//  * 16 lanes reading rows perm_row(u, 0..15) at one chunk hit 16 positions;
 //  * 32 lanes of ds_read_b64_tr_b16 reading rows 8a + 4q + (0..3), a in {0,1} or
-//    {2,3}, at chunks 2t and 2t+1 hit 32 distinct 8-byte slots;
+//    {2,3}, at chunks 2t and 2t+1 hit 32 distinct 8-byte slots (measured
+//    conflict-free on gfx950);
 //  * 16 lanes writing 16 consecutive chunks of one row hit 16 positions.
-// For narrower rows the value is masked to the row's chunk count (correct, not
-// conflict-optimised).
+// ds_read_b128 of rows perm_row(u, 0..15) does conflict under it (2-way, measured):
+// tiles read both ways use swz_kv below.  For narrower rows the value is masked to
+// the row's chunk count (correct, not conflict-optimised).
 __device__ __forceinline__ int swz_rows(int r) {
   return ((r >> 4) & 1) | ((r & 3) << 1) | (((r >> 3) & 1) << 3);
 }
