@@ -323,6 +323,89 @@ def test_shortconv2d_delta_and_box_closed_forms(rng):
     np.testing.assert_array_equal(got, np.array([[3, 4, 5], [6, 7, 8], [0, 0, 0]], float))
 
 
+# ------------------------------------------------ the whole layer's composition
+def _shift_down(v, frames, tpf, sp, gh, gw):
+    """V with every frame's patch grid moved down one row (row 0 zero), special rows
+    kept: what a 3x3 tap at (dy, dx) = (-1, 0) alone computes, built by indexing."""
+    out = v.copy()
+    for f in range(frames):
+        base = f * tpf + sp
+        img = v[base:base + gh * gw].reshape(gh, gw, -1)
+        moved = np.zeros_like(img)
+        moved[1:] = img[:-1]
+        out[base:base + gh * gw] = moved.reshape(gh * gw, -1)
+    return out
+
+
+def _layer_conv_case(rng):
+    H, d, m, frames, sp, gh, gw = 2, 8, 12, 2, 2, 3, 4
+    tpf = sp + gh * gw
+    n = frames * tpf
+    w, k, v, q, eta = _layer_inputs(rng, H, d, m, n, 9, scale=0.3)
+    wc = np.zeros((H * d, 3, 3))
+    wc[:, 0, 1] = 1.0                       # w[dy+1, dx+1] at dy = -1: V'[y, x] = V[y-1, x]
+    geo = dict(frames=frames, tokens_per_frame=tpf, n_special=sp, grid_h=gh, grid_w=gw)
+    return (H, d, m), w, k, v, q, eta, wc, geo
+
+
+def test_layer_conv_feeds_shifted_values_to_the_update_only(rng):
+    # VGG-T3 关键设计 2: V' = ShortConv2D(V) replaces V as the update's target, K and
+    # the queries are untouched.  With a one-tap shift the expected V' is built by
+    # indexing, and the one-step result is rebuilt from independent routines: torch
+    # autograd of the loss on (K, V') for G, the SVD closed form for NS(G), and a
+    # per-token loop of f_W^ for O.
+    (H, d, m), w, k, v, q, eta, wc, geo = _layer_conv_case(rng)
+    lr = 0.05
+    o, w_hat, g, ns = oracle.layer(*w, k, v, eta, q, lr, 1, conv=dict(wconv=wc, **geo))
+    vs = _shift_down(v, geo["frames"], geo["tokens_per_frame"], geo["n_special"], geo["grid_h"], geo["grid_w"])
+    assert not np.array_equal(vs, v)
+    for h in range(H):
+        c = slice(h * d, (h + 1) * d)
+        t = [torch.tensor(x[h], requires_grad=True) for x in w]
+        kt, vt, et = torch.from_numpy(k[:, c]), torch.from_numpy(vs[:, c]), torch.from_numpy(eta[h])
+        f = (torch.nn.functional.silu(kt @ t[0].T) * (kt @ t[1].T)) @ t[2].T
+        (-(et * (f * vt).sum(1)).sum()).backward()
+        for j in range(3):
+            gref = t[j].grad.numpy()
+            assert rel_fro(g[j][h], gref) <= 1e-12
+            u, s, vh = np.linalg.svd(gref, full_matrices=False)
+            nref = u @ np.diag(_p5(s / (np.linalg.norm(gref) + 1e-7))) @ vh
+            assert rel_fro(ns[j][h], nref) <= 1e-10
+            assert rel_fro(w_hat[j][h], w[j][h] - lr * nref) <= 1e-12
+        w1h, w3h, w2h = (x[h] for x in w_hat)
+        for i in range(q.shape[0]):
+            x = q[i, c]
+            z1, z3 = w1h @ x, w3h @ x
+            ref = w2h @ (z1 / (1.0 + np.exp(-z1)) * z3)
+            np.testing.assert_allclose(o[i, c], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_layer_two_steps_equals_update_then_apply_on_hand_shifted_values(rng):
+    # Two steps with conv: the same as update(K, shifted V) twice, then apply with the
+    # final W.  Each plausible miswiring (conv on K, the unconvolved V, apply with W0)
+    # gives a different result, which the last assertions confirm.
+    (H, d, m), w, k, v, q, eta, wc, geo = _layer_conv_case(rng)
+    lr = 0.05
+    o, w_hat, g, ns = oracle.layer(*w, k, v, eta, q, lr, 2, conv=dict(wconv=wc, **geo))
+    vs = _shift_down(v, geo["frames"], geo["tokens_per_frame"], geo["n_special"], geo["grid_h"], geo["grid_w"])
+    w_ref, g_ref, ns_ref = oracle.update(*w, k, vs, eta, lr, 2)
+    for a, b in zip(w_hat + g + ns, w_ref + g_ref + ns_ref):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(o, oracle.apply(*w_ref, q))
+    ks = _shift_down(k, geo["frames"], geo["tokens_per_frame"], geo["n_special"], geo["grid_h"], geo["grid_w"])
+    assert rel_fro(oracle.update(*w, ks, v, eta, lr, 2)[1][0], g[0]) > 1e-3       # conv on K instead
+    assert rel_fro(oracle.update(*w, k, v, eta, lr, 2)[1][0], g[0]) > 1e-3        # V not convolved
+    assert rel_fro(oracle.apply(*w, q), o) > 1e-3                                  # apply with W0
+    # a centre-tap (identity) kernel makes the conv branch a no-op
+    ident = np.zeros_like(wc)
+    ident[:, 1, 1] = 1.0
+    o_id, w_id, _, _ = oracle.layer(*w, k, v, eta, q, lr, 2, conv=dict(wconv=ident, **geo))
+    o_nc, w_nc, _, _ = oracle.layer(*w, k, v, eta, q, lr, 2)
+    np.testing.assert_array_equal(o_id, o_nc)
+    for a, b in zip(w_id, w_nc):
+        np.testing.assert_array_equal(a, b)
+
+
 # ------------------------------------------- ZipMap stabilisers (optional forms)
 def test_norm_preserving_step_hand_example():
     # ||W|| = 5, W - Delta = diag(0, 4) with norm 4, so W^ = diag(0, 5)

@@ -3,6 +3,7 @@ import json
 import os
 
 import numpy as np
+import pytest
 import torch
 
 from test_weight_layers_amd.configs import CONFIGS, VGGT_TOKENS
@@ -45,14 +46,15 @@ def test_bf16_rounding_is_nearest_even():
     assert np.array_equal(rne, y.view(torch.int16).numpy().view(np.uint16))
 
 
-def test_golden_c1_oracle_unchanged():
+@pytest.mark.parametrize("name", ["c1", "c3tiny_conv"])
+def test_golden_oracle_unchanged(name):
     import importlib.util
     spec = importlib.util.spec_from_file_location("make_golden", os.path.join(HERE, "golden", "make_golden.py"))
     mg = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mg)
-    with open(os.path.join(HERE, "golden", "c1_oracle.json")) as f:
+    with open(os.path.join(HERE, "golden", mg.FILES[name])) as f:
         stored = json.load(f)["tensors"]
-    now = mg.compute()
+    now = mg.compute(name)
     for s, n in zip(stored, now):
         assert s["name"] == n["name"] and s["shape"] == n["shape"]
         assert abs(s["fro"] - n["fro"]) <= 1e-12 * max(1.0, abs(s["fro"]))
