@@ -18,8 +18,15 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Shapes.  H heads, per-head width d, SwiGLU hidden width m.  Supported: d in
- *   {64, 128, 256, 512, 768, 1024}, m a positive multiple of 64.
+ * Shapes.  H heads, per-head width d, SwiGLU hidden width m.  Supported: d a
+ *   multiple of 64 in [64, 1024], m a positive multiple of 64 (the 64-wide MFMA
+ *   tile); anything else returns TTT_EUNSUPPORTED.  Kernel choice (results agree
+ *   within the bf16 tolerance either way): bf16 tokens with d in {64, 128, 256} run
+ *   the fused fast kernels; bf16 with d in {512, 768, 1024} and m % 256 == 0 run the
+ *   wide-head kernels (the gradient and apply split at the hidden layer into dense
+ *   products); every other shape, and fp32 tokens, run the general kernels, which
+ *   read their operands from L1/L2 and are roughly 20-40x slower than the fast or
+ *   wide kernels on the same work (about 20 TFLOP/s at d = 1024, m = 2048).
  * Fast weights, always fp32, caller-owned DEVICE memory, contiguous:
  *   w1, w3: [H][m][d]   (row j of head h multiplies the key: z = W1 k)
  *   w2:     [H][d][m]   (f_W(x) = W2 (SiLU(W1 x) o (W3 x)))

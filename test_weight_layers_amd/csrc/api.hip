@@ -76,12 +76,15 @@ int run(int kind, const char *what, hipStream_t s, F &&f) {
 }
 
 // ----------------------------------------------------------------- checks
-bool d_supported(int d) { return d == 64 || d == 128 || d == 256 || d == 512 || d == 768 || d == 1024; }
+// Every head width that is a multiple of the 64-wide tile, up to 1024.  d in {64, 128,
+// 256} (bf16) runs the fused fast kernels, bf16 d in {512, 768, 1024} with m % 256 == 0
+// the wide-head kernels, everything else the general kernels.
+bool d_supported(int d) { return d >= 64 && d <= 1024 && d % 64 == 0; }
 
 int check_shape(int heads, int d, int m, int dtype) {
   if (heads < 1) return fail(TTT_EINVAL, "heads must be >= 1 (got %d)", heads);
   if (dtype != TTT_F32 && dtype != TTT_BF16) return fail(TTT_EUNSUPPORTED, "unknown dtype %d", dtype);
-  if (!d_supported(d)) return fail(TTT_EUNSUPPORTED, "d=%d not in {64,128,256,512,768,1024}", d);
+  if (!d_supported(d)) return fail(TTT_EUNSUPPORTED, "d=%d is not a multiple of 64 in [64, 1024]", d);
   if (m < 64 || m % 64 != 0) return fail(TTT_EUNSUPPORTED, "m=%d must be a positive multiple of 64", m);
   return TTT_OK;
 }
@@ -268,7 +271,7 @@ int gradient_pass(const UpdatePlan &P, const GradOps &ops, const void *k, const 
   gp.k = k, gp.v = v, gp.ld = ld, gp.eta = eta, gp.eta_hs = eta_hs;
   gp.w1 = ops.w1, gp.w3 = ops.w3, gp.w2t = ops.w2t;
   gp.part = part, gp.n = P.n, gp.nblk = P.nblk;
-  gp.heads = P.H, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
+  gp.heads = P.H, gp.d = P.d, gp.m = P.m, gp.splits = P.splits, gp.dchunks = P.dchunks, gp.xcd_map = P.xcd;
   // the hidden tiles of a token range keep pace through these counters (see the kernel)
   if (P.fast && P.xcd) gp.group_sync = reinterpret_cast<unsigned *>(ws + P.off_sync);
   return run(TTT_K_GRAD, "gradient", s, [&] {
@@ -425,7 +428,7 @@ int do_apply(int H, int d, int m, W3 w, const void *q, int64_t ldq, void *o, int
     return run(TTT_K_APPLY, "apply", s, [&] { return launch_big_apply(bp, s); });
   }
   ApplyParams ap{};
-  ap.q = q, ap.ldq = ldq, ap.o = o, ap.ldo = ldo, ap.nq = nq, ap.heads = H, ap.m = m;
+  ap.q = q, ap.ldq = ldq, ap.o = o, ap.ldo = ldo, ap.nq = nq, ap.heads = H, ap.d = d, ap.m = m;
   ap.dchunks = fast ? 1 : d / apply_general_dc(d, bf16);
   if (bf16) {
     // the fast kernel reads W2 transposed ([H][m][d]), the general one as stored

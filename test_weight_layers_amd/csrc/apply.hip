@@ -13,10 +13,7 @@ namespace ttt {
 namespace {
 
 constexpr int kHidChunk = 32;
-#ifndef APPLY_WAVES
-#define APPLY_WAVES 8
-#endif
-constexpr int kApplyWaves = APPLY_WAVES;   // waves (of 32 tokens) per fast workgroup
+constexpr int kApplyWaves = 8;   // waves (of 32 tokens) per fast workgroup
 
 // ---------------------------------------------------------------- fast path
 // bf16, D <= 256.  A workgroup owns 32 WV tokens of one head (32 per wave, WV
@@ -198,13 +195,15 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
 }
 
 // ------------------------------------------------------------- general path
-// Any supported d, fp32 or bf16: 16 tokens per wave, 64 per workgroup, one
-// output d-chunk of DC columns per workgroup; operands read from global
-// memory (L1/L2 resident).  The first contraction is recomputed per d-chunk.
-template <typename T, int D, int DC>
+// Any supported d (a multiple of 64 up to 1024, taken at run time), fp32 or bf16:
+// 16 tokens per wave, 64 per workgroup, one output d-chunk of DC columns per
+// workgroup; operands read from global memory (L1/L2 resident).  The first
+// contraction is recomputed per d-chunk.
+template <typename T, int DC>
 __global__ __launch_bounds__(256) void apply_general_kernel(ApplyParams p) {
   using F = typename FragOf<T>::type;
-  constexpr int KC = D / 32, DT = DC / 16;
+  constexpr int DT = DC / 16;
+  const int D = p.d, KC = D / 32;
   const int h = blockIdx.x % p.heads;
   int64_t rest = blockIdx.x / p.heads;
   const int dc = rest % p.dchunks;
@@ -260,33 +259,24 @@ __global__ __launch_bounds__(256) void apply_general_kernel(ApplyParams p) {
     for (int r = 0; r < 4; ++r) O[16 * dt + r] = from_f32<T>(acc[dt][r]);
 }
 
-template <typename T, int D>
-hipError_t launch_general(const ApplyParams &p, hipStream_t s) {
-  constexpr int DC = (D < 128) ? D : 128;
+template <typename T>
+hipError_t launch_general_d(const ApplyParams &p, int d, hipStream_t s) {
+  if (d < 64 || d > 1024 || d % 64 != 0 || p.d != d) return hipErrorInvalidValue;
   const int64_t tiles = (p.nq + 63) / 64;
   const int64_t grid = tiles * p.heads * p.dchunks;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((apply_general_kernel<T, D, DC>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  if (apply_general_dc(d, sizeof(T) == 2) == 128)
+    hipLaunchKernelGGL((apply_general_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((apply_general_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_general_d(const ApplyParams &p, int d, hipStream_t s) {
-  switch (d) {
-    case 64: return launch_general<T, 64>(p, s);
-    case 128: return launch_general<T, 128>(p, s);
-    case 256: return launch_general<T, 256>(p, s);
-    case 512: return launch_general<T, 512>(p, s);
-    case 768: return launch_general<T, 768>(p, s);
-    case 1024: return launch_general<T, 1024>(p, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool apply_fast_supported(int d, bool bf16) { return bf16 && (d == 64 || d == 128 || d == 256); }
-int apply_general_dc(int d, bool) { return d < 128 ? d : 128; }
+// output d-chunk of the general kernel: 128 columns where d allows, else 64
+int apply_general_dc(int d, bool) { return d % 128 == 0 ? 128 : 64; }
 
 hipError_t launch_apply(const ApplyParams &p, int d, bool bf16, bool fast, hipStream_t s) {
   if (fast) {

@@ -563,8 +563,9 @@ __global__ __launch_bounds__(512) void big_out_kernel(BigApplyParams p) {
 
 }  // namespace
 
+// the tiles span 256 columns of d (contraction mode 1, output kernel) and 256 hidden units
 bool big_supported(int d, int m, bool bf16) {
-  return bf16 && (d == 512 || d == 768 || d == 1024) && m % 256 == 0;
+  return bf16 && d >= 512 && d <= 1024 && d % 256 == 0 && m % 256 == 0;
 }
 int64_t big_pad_tokens(int64_t n) { return (n + 767) / 768 * 768; }
 

@@ -15,10 +15,12 @@
 // that a second kernel sums in fixed split order (deterministic).
 //
 // Per 32-token block a wave computes z1, z3, p for its 16 hidden units x 32
-// tokens (MFMA, tokens as rows), applies the SwiGLU backward in registers, and
-// feeds dZ1, dZ3, H' straight back into the MFMA as operands: the tokens'
-// row order is permuted (perm_row) so that the accumulator layout of the first
-// product is the operand layout of the second, with no LDS round trip.
+// tokens (MFMA, tokens as rows) and applies the SwiGLU backward in registers.
+// The tokens' row order is permuted (perm_row) so that the accumulator layout of
+// the first product is the operand layout of the contractions: dZ1, dZ3, H' are
+// packed to bf16 operands as they are.  In the general kernel the same wave then
+// runs the contractions from registers; in the fast kernel the packed operands
+// pass through a small LDS buffer to the waves that hold the accumulators.
 #include "common.h"
 #include "kernels.h"
 
@@ -391,14 +393,15 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
 }
 
 // ------------------------------------------------------------- general path
-// Any supported d, fp32 or bf16.  The d-reductions read K, V and the weights
+// Any supported d (a multiple of 64 up to 1024, taken at run time), fp32 or bf16.  The d-reductions read K, V and the weights
 // straight from global memory (L1/L2 resident); only the transposed K, V
 // columns of this workgroup's output d-chunk go through LDS.  The forward is
 // recomputed for every d-chunk.
-template <typename T, int D, int DC>
+template <typename T, int DC>
 __global__ __launch_bounds__(256) void grad_general_kernel(GradParams p) {
   using F = typename FragOf<T>::type;
-  constexpr int KC = D / 32;
+  const int D = p.d;
+  const int KC = D / 32;
   constexpr int DT = DC / 16;
   constexpr int PAD = 16 / sizeof(T);         // keeps 16-byte aligned rows
   constexpr int RS = kTokBlock + PAD;         // LDS row stride (elements)
@@ -503,24 +506,14 @@ __global__ __launch_bounds__(256) void grad_general_kernel(GradParams p) {
     }
 }
 
-template <typename T, int D>
-hipError_t launch_general(const GradParams &p, int grid, hipStream_t s) {
-  constexpr int DC = (sizeof(T) == 2) ? (D < 128 ? D : 128) : (D < 64 ? D : 64);
-  hipLaunchKernelGGL((grad_general_kernel<T, D, DC>), dim3(grid), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
 template <typename T>
 hipError_t launch_general_d(const GradParams &p, int d, int grid, hipStream_t s) {
-  switch (d) {
-    case 64: return launch_general<T, 64>(p, grid, s);
-    case 128: return launch_general<T, 128>(p, grid, s);
-    case 256: return launch_general<T, 256>(p, grid, s);
-    case 512: return launch_general<T, 512>(p, grid, s);
-    case 768: return launch_general<T, 768>(p, grid, s);
-    case 1024: return launch_general<T, 1024>(p, grid, s);
-  }
-  return hipErrorInvalidValue;
+  if (d < 64 || d > 1024 || d % 64 != 0 || p.d != d) return hipErrorInvalidValue;
+  if (grad_general_dc(d, sizeof(T) == 2) == 128)
+    hipLaunchKernelGGL((grad_general_kernel<T, 128>), dim3(grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((grad_general_kernel<T, 64>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(unsigned *p, int n) {
@@ -538,10 +531,8 @@ hipError_t launch_zero_u32(unsigned *p, int n, hipStream_t s) {
 
 bool grad_fast_supported(int d, bool bf16) { return bf16 && (d == 64 || d == 128 || d == 256); }
 
-int grad_general_dc(int d, bool bf16) {
-  if (bf16) return d < 128 ? d : 128;
-  return d < 64 ? d : 64;
-}
+// output d-chunk of the general kernel: 128 columns for bf16 where d allows, else 64
+int grad_general_dc(int d, bool bf16) { return bf16 && d % 128 == 0 ? 128 : 64; }
 
 hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int grid, hipStream_t s) {
   if (fast) {

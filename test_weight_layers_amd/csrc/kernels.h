@@ -20,7 +20,7 @@ struct GradParams {
   const void *w2t;           // [H][m][d] transposed W2
   float *part;               // [splits][3][H][m*d] fp32 partial gradients
   int64_t n, nblk;           // tokens, ceil(n / kTokBlock)
-  int heads, m, splits, dchunks, xcd_map;
+  int heads, d, m, splits, dchunks, xcd_map;
   unsigned *group_sync;      // fast kernel: [H * splits] progress counters, zero at launch (or null)
 };
 
@@ -33,11 +33,12 @@ struct ApplyParams {
   const void *w2;            // [H][d][m] (general kernels)
   const void *w2t;           // [H][m][d] transposed W2 (fast kernel)
   int64_t nq;
-  int heads, m, dchunks;
+  int heads, d, m, dchunks;
 };
 
-// Kernel families.  `fast` variants: bf16 tokens with d <= 256 (LDS-staged,
-// register-resident weights); `general` variants: any supported d, fp32 or bf16.
+// Kernel families.  `fast` variants: bf16 tokens with d in {64, 128, 256}
+// (LDS-staged, register-resident weights); `general` variants: any supported d
+// (a multiple of 64 up to 1024), fp32 or bf16.
 bool grad_fast_supported(int d, bool bf16);
 int grad_general_dc(int d, bool bf16);      // output d-chunk width of the general kernel
 hipError_t launch_grad(const GradParams &p, int d, bool bf16, bool fast, int grid, hipStream_t s);
@@ -136,8 +137,8 @@ struct GateParams {
 int64_t gate_tiles(int64_t n);
 hipError_t launch_gate(const GateParams &p, bool bf16, hipStream_t s);
 
-// Wide heads (bf16, d in {512, 768, 1024}, m % 256 == 0): the update and apply
-// split at the hidden layer into dense contractions (bigd.hip).
+// Wide heads (bf16, d a multiple of 256 from 512 to 1024, m % 256 == 0): the
+// update and apply split at the hidden layer into dense contractions (bigd.hip).
 bool big_supported(int d, int m, bool bf16);
 int64_t big_pad_tokens(int64_t n);          // token rows of the intermediates (multiple of 768)
 int big_contract_tiles(int d, int m, int mode);

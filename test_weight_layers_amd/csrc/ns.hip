@@ -5,8 +5,11 @@
 // Newton-Schulz (ZipMap 关键设计 3: Delta <- NewtonSchulz(g); VGG-T3 and tttLRM
 // name the Muon optimiser): X = G / (||G||_F + eps), transposed while it has more
 // rows than columns, then five times  A = X X^T,  B = b A + c A A,  X = a X + B X
-// with Muon's quintic coefficients (a, b, c) = (3.4445, -4.7750, 2.0315).  All of
-// it runs in fp32 (fp32 MFMA); only the three small GEMMs per iteration are
+// with Muon's quintic coefficients (a, b, c) = (3.4445, -4.7750, 2.0315).  The
+// iterates and every product's accumulation are fp32.  In fp32 token mode the
+// products run on fp32 MFMA; in bf16 token mode each fp32 operand is split into
+// bf16 hi + lo parts and the products hi*hi + hi*lo + lo*hi run on bf16 MFMA with
+// fp32 accumulation (about 16 significant bits per operand).  Every product is
 // batched over the 3*H gradient matrices.
 #include "common.h"
 #include "kernels.h"

@@ -115,6 +115,38 @@ def _weights(w: Sequence[torch.Tensor]) -> Tuple[int, int, int]:
     return H, d, m
 
 
+def _eta_stride(eta: torch.Tensor, H: int, n: int, device, on_gpu: bool = True) -> int:
+    """Head stride of the rates: [H, >=n] with unit token stride, or [>=n] shared by every head."""
+    if eta.dtype != torch.float32:
+        raise ValueError("eta must be float32")
+    if on_gpu:
+        if not eta.is_cuda or (device is not None and eta.device != torch.device(device)):
+            raise ValueError("eta must be on the same GPU as the tokens")
+    elif eta.is_cuda:
+        raise ValueError("eta must be in host memory")
+    if eta.dim() == 2:
+        if eta.shape[0] != H or eta.shape[1] < n or (n > 1 and eta.stride(1) != 1) or eta.stride(0) < 0:
+            raise ValueError(f"eta must be [H={H}, >={n}] with unit token stride")
+        return eta.stride(0)
+    if eta.dim() == 1:
+        if eta.shape[0] < n or (n > 1 and eta.stride(0) != 1):
+            raise ValueError(f"eta must be [>={n}] with unit stride")
+        return 0
+    raise ValueError("eta must be [H, N] or [N]")
+
+
+def _same_rows(t: torch.Tensor, like: torch.Tensor, rows: int, width: int, name: str) -> int:
+    """`t` is a [rows, >=width] tensor of like's dtype and device with unit column stride;
+    returns its row stride."""
+    if t.dtype != like.dtype:
+        raise ValueError(f"{name} must have dtype {like.dtype}, got {t.dtype}")
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}")
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] < width or t.stride(1) != 1:
+        raise ValueError(f"{name} must be [{rows}, >={width}] with unit column stride, got {tuple(t.shape)}")
+    return t.stride(0)
+
+
 def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return None
@@ -156,19 +188,13 @@ def update(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: tor
     if v.dtype != k.dtype or v.shape != k.shape or v.stride() != k.stride():
         raise ValueError("k and v must share dtype, shape and strides")
     ld = _rows(k, "k")
-    if eta.dtype != torch.float32 or not eta.is_cuda:
-        raise ValueError("eta must be a float32 GPU tensor")
-    if eta.dim() == 2:
-        if eta.shape[0] != H or eta.shape[1] < n or eta.stride(1) != 1:
-            raise ValueError("eta must be [H, N] with unit token stride")
-        ehs = eta.stride(0)
-    elif eta.dim() == 1 and eta.shape[0] >= n:
-        ehs = 0
-    else:
-        raise ValueError("eta must be [H, N] or [N]")
+    if k.shape[1] < H * d:
+        raise ValueError(f"k rows must hold H*d = {H * d} columns")
+    ehs = _eta_stride(eta, H, n, k.device)
     for t, name in ((grad_out, "grad_out"), (ns_out, "ns_out")):
-        if t is not None and (t.dtype != torch.float32 or t.numel() != 3 * H * d * m or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous float32 tensor of 3*H*m*d elements")
+        if t is not None and (t.dtype != torch.float32 or t.numel() != 3 * H * d * m or not t.is_contiguous()
+                              or t.device != k.device):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of 3*H*m*d elements on k's GPU")
     need = update_workspace_bytes(H, d, m, n, k.dtype)
     if workspace is None:
         workspace = _workspace(need, k.device)
@@ -202,12 +228,13 @@ def update_host(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta
         raise ValueError("update_host takes k, v and eta in host memory")
     if v.dtype != k.dtype or v.shape != k.shape or v.stride() != k.stride() or k.dim() != 2 or k.stride(1) != 1:
         raise ValueError("k and v must be 2-D host tensors sharing dtype, shape and strides")
-    if eta.dtype != torch.float32:
-        raise ValueError("eta must be float32")
-    ehs = eta.stride(0) if eta.dim() == 2 else 0
+    if k.shape[1] < H * d:
+        raise ValueError(f"k rows must hold H*d = {H * d} columns")
+    ehs = _eta_stride(eta, H, n, None, on_gpu=False)
     for t, name in ((grad_out, "grad_out"), (ns_out, "ns_out")):
-        if t is not None and (t.dtype != torch.float32 or t.numel() != 3 * H * d * m or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous float32 tensor of 3*H*m*d elements")
+        if t is not None and (t.dtype != torch.float32 or t.numel() != 3 * H * d * m or not t.is_contiguous()
+                              or t.device != w[0].device):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of 3*H*m*d elements on the weights' GPU")
     ld = k.stride(0)
     need = update_host_workspace_bytes(H, d, m, batch, ld, k.dtype)
     if workspace is None:
@@ -226,9 +253,11 @@ def apply(w: Sequence[torch.Tensor], q: torch.Tensor, out: Optional[torch.Tensor
     H, d, m = _weights(w)
     code = _dtype_code(q)
     ldq = _rows(q, "q")
+    if q.shape[1] < H * d:
+        raise ValueError(f"q rows must hold H*d = {H * d} columns")
     if out is None:
         out = torch.empty((q.shape[0], H * d), dtype=q.dtype, device=q.device)
-    ldo = _rows(out, "out")
+    ldo = _same_rows(out, q, q.shape[0], H * d, "out")
     need = apply_workspace_bytes(H, d, m, q.shape[0], q.dtype)
     if workspace is None:
         workspace = _workspace(need, q.device)
@@ -268,14 +297,17 @@ def stream(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: tor
     H, d, m = _weights(w)
     code = _dtype_code(k)
     n = k.shape[0]
-    if q.shape[0] != n:
-        raise ValueError("stream needs one query row per token")
     ld = _rows(k, "k")
-    ldq = _rows(q, "q")
+    if k.shape[1] < H * d:
+        raise ValueError(f"k rows must hold H*d = {H * d} columns")
+    if v.stride() != k.stride():
+        raise ValueError("k and v must share strides")
+    _same_rows(v, k, n, H * d, "v")
+    ldq = _same_rows(q, k, n, H * d, "q")
     if out is None:
         out = torch.empty((n, H * d), dtype=q.dtype, device=q.device)
-    ldo = _rows(out, "out")
-    ehs = eta.stride(0) if eta.dim() == 2 else 0
+    ldo = _same_rows(out, k, n, H * d, "out")
+    ehs = _eta_stride(eta, H, n, k.device)
     need = stream_workspace_bytes(H, d, m, chunk, k.dtype)
     if workspace is None:
         workspace = _workspace(need, k.device)
@@ -296,9 +328,13 @@ def output_gate(o: torch.Tensor, wg: torch.Tensor, gamma: torch.Tensor, eps: flo
     if gamma.dtype != torch.float32 or tuple(gamma.shape) != (C,) or not gamma.is_contiguous() or not gamma.is_cuda:
         raise ValueError("gamma must be a contiguous float32 [C] GPU tensor")
     ldi = _rows(o, "o")
+    if o.shape[1] < C:
+        raise ValueError(f"o rows must hold C = {C} columns")
+    if wg.device != o.device or gamma.device != o.device:
+        raise ValueError("wg and gamma must be on o's GPU")
     if out is None:
         out = torch.empty((o.shape[0], C), dtype=o.dtype, device=o.device)
-    ldo = _rows(out, "out")
+    ldo = _same_rows(out, o, o.shape[0], C, "out")
     _check(load().ttt_output_gate(C, o.data_ptr(), ldi, wg.data_ptr(), gamma.data_ptr(), float(eps), out.data_ptr(),
                                   ldo, o.shape[0], code, _stream()))
     return out

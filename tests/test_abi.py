@@ -1,10 +1,16 @@
 """The C-ABI library loads, exports every symbol the header declares, and its
-host-side argument checks and workspace queries work without a GPU."""
+host-side argument checks and workspace queries work without a GPU.
+
+The argument-error tests pass made-up addresses that every check rejects before
+any launch.  They run only where no GPU is visible: on a machine with a GPU a
+regressed check would launch kernels on those addresses.
+"""
 import ctypes
 import os
 import re
 
 import pytest
+import torch
 
 from test_weight_layers_amd import ttt
 
@@ -33,6 +39,11 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(ttt.EXPORTS)
 
 
+# torch.cuda.device_count() counts devices without initialising the HIP runtime
+cpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                              reason="passes made-up device addresses; CPU-only by design")
+
+
 def _ws(lib, fn, *args):
     out = ctypes.c_size_t()
     st = getattr(lib, fn)(*args, ctypes.byref(out))
@@ -52,8 +63,19 @@ def test_workspace_queries(lib):
     assert st == 0 and s > 0
 
 
+@pytest.mark.parametrize("d", [64, 192, 320, 384, 640, 960, 1024])
+def test_workspace_query_accepts_every_multiple_of_64(lib, d):
+    for dt in (ttt.TTT_BF16, ttt.TTT_F32):
+        st, b = _ws(lib, "ttt_update_workspace_bytes", 2, d, 128, 5000, dt)
+        assert st == 0 and b >= 3 * 2 * d * 128 * 4
+        st, _ = _ws(lib, "ttt_apply_workspace_bytes", 2, d, 128, 5000, dt)
+        assert st == 0
+
+
 @pytest.mark.parametrize("args,code", [
     ((4, 100, 512, 10, ttt.TTT_BF16), -2),     # d unsupported
+    ((4, 1088, 512, 10, ttt.TTT_BF16), -2),    # d above 1024
+    ((4, 0, 512, 10, ttt.TTT_BF16), -2),       # d zero
     ((4, 256, 500, 10, ttt.TTT_BF16), -2),     # m not a multiple of 64
     ((0, 256, 512, 10, ttt.TTT_BF16), -1),     # heads
     ((4, 256, 512, -1, ttt.TTT_BF16), -1),     # n < 0
@@ -65,6 +87,7 @@ def test_workspace_query_rejects_bad_shapes(lib, args, code):
     assert len(lib.ttt_last_error()) > 0
 
 
+@cpu_only
 def test_update_argument_errors_return_before_any_launch(lib):
     # null weights
     st = lib.ttt_update(1, 64, 128, None, None, None, None, None, None, None, None, 64, None, 0, 10, 0.01, 1,
@@ -89,6 +112,7 @@ def test_update_argument_errors_return_before_any_launch(lib):
     assert st == -1 and b"overlap" in lib.ttt_last_error()
 
 
+@cpu_only
 def test_apply_and_conv_argument_errors(lib):
     fake = 1 << 20
     st = lib.ttt_apply(1, 64, 128, fake, fake, fake, fake, 64, fake + 16, 64, 10, ttt.TTT_F32, None, 0, None)
@@ -105,6 +129,7 @@ def test_apply_and_conv_argument_errors(lib):
     assert st == -1
 
 
+@cpu_only
 def test_update_ex_stream_ex_and_gate_argument_errors(lib):
     fake = 1 << 20   # never dereferenced: every check below fails first
     # unknown flag bits
@@ -129,6 +154,7 @@ def test_update_ex_stream_ex_and_gate_argument_errors(lib):
     assert lib.ttt_output_gate(64, None, 64, None, None, 1e-6, None, 64, 0, ttt.TTT_BF16, None) == 0
 
 
+@cpu_only
 def test_update_host_argument_errors(lib):
     fake = 1 << 20
     st, nb = _ws(lib, "ttt_update_host_workspace_bytes", 4, 256, 512, 4096, 1024, ttt.TTT_BF16)

@@ -74,14 +74,16 @@ def test_other_fast_widths(d, m):
     _check(cfg_like("c4", heads=2, d=d, m=m), n=777, nq_extra=3)
 
 
-def test_tttlrm_width_768_general():
+def test_tttlrm_width_768():
+    # the tttLRM head (d = m = 768): the wide-head kernels (big_* in bigd.hip)
     from test_weight_layers_amd.configs import CONFIGS
     _check(CONFIGS["c2"], n=1500, nq_extra=300)
 
 
 def test_zipmap_single_head_1024_2048():
     # the ZipMap layer's own shape (one head, d = 1024, m = 2048, state 6 d^2): the
-    # general kernels, the 1024 x 2048 Newton-Schulz products, a ragged token tail
+    # wide-head kernels (bigd.hip), the 1024 x 2048 Newton-Schulz products, a ragged
+    # token tail; the full-size workload is checked in test_gpu_fullsize.py
     from test_weight_layers_amd.configs import CONFIGS
     _check(CONFIGS["zipmap1h"], n=1500, nq_extra=77)
 
@@ -94,6 +96,14 @@ def test_wide_heads(shape, general):
     # the oracle: ragged token tails, fewer tokens than one 256-row tile, Nq > N
     H, d, m, n, extra = shape
     _check(cfg_like("c4", heads=H, d=d, m=m), n=n, nq_extra=extra, general=general)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d,m", [(192, 128), (320, 256), (384, 512), (640, 192), (512, 320)])
+def test_every_multiple_of_64_width(d, m, dtype):
+    # head widths outside the fast and wide sets (and a wide d with m % 256 != 0) run
+    # the general kernels with d taken at run time
+    _check(cfg_like("c4", heads=2, d=d, m=m, dtype=dtype), n=333, nq_extra=17)
 
 
 def test_two_inner_steps_with_conv():
@@ -118,8 +128,10 @@ def test_many_splits_and_single_split_agree():
 
 @pytest.mark.parametrize("case", ["c1-fp32", "vggt-2step", "d64-m128", "d768"])
 def test_fused_and_unfused_optimiser_step(case):
-    # one cooperative launch (reduce + Newton-Schulz + step) against the separate
-    # launches: both against the oracle, and against each other
+    # the folded optimiser step (split sum, Newton-Schulz with the Frobenius scale
+    # folded into its first products, the step in the last product's epilogue: 16
+    # launches) against the unfolded sequence of separate kernels: both against the
+    # oracle, and against each other
     from test_weight_layers_amd.configs import CONFIGS
     cfg, kw = {"c1-fp32": (CONFIGS["c1"], dict(steps=2)),
                "vggt-2step": (cfg_like("c4", heads=2), dict(n=1500, nq_extra=0, steps=2)),
