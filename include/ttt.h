@@ -139,6 +139,36 @@ int ttt_update_ex(int32_t heads, int32_t d, int32_t m,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ttt_update_noalloc -- ttt_update_ex without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine, no timing events even when
+ * ttt_profile_enable is on); it takes its scratch from a library-owned device array of
+ * ttt_noalloc_scratch_bytes() bytes (128 MiB), which every GPU that runs the library
+ * holds from the first call on that device until the process ends.
+ *
+ * Every argument means what it means for ttt_update_ex, and the kernels and the
+ * result are the same: bit-identical to ttt_update_ex on the same inputs.
+ * Limit: the update's scratch (ttt_update_workspace_bytes for the same shapes) must
+ *   fit the array: about 87 MiB for 4 heads of 256 with hidden 512 (any n), 1.4 MiB
+ *   for one 64/128 head.  The wide-head path's intermediates grow with n and do not
+ *   fit at large n.  A larger need returns TTT_EWORKSPACE before anything runs.
+ * Sharing: every call on one GPU uses that GPU's one array, and the array keeps the
+ *   last call's contents (each call clears what it needs at zero).  Calls that may
+ *   overlap on one GPU (other host threads, other streams) race on it: the caller
+ *   must serialise them.
+ */
+int ttt_update_noalloc(int32_t heads, int32_t d, int32_t m,
+                       const float *w1, const float *w3, const float *w2,
+                       float *w1_out, float *w3_out, float *w2_out,
+                       const void *k, const void *v, int64_t ld_kv,
+                       const float *eta, int64_t eta_head_stride,
+                       int64_t n, float lr, int32_t steps, int32_t dtype, uint32_t flags,
+                       float *grad_out, float *ns_out, void *stream);
+/* Size of the array ttt_update_noalloc works in (bytes). */
+int ttt_noalloc_scratch_bytes(size_t *bytes);
+
+/*
  * ttt_update_host -- ttt_update_ex with K, V and eta in HOST memory, streamed to
  * the GPU in batches of `batch` tokens ([VGG-T3] 关键发现 2 and 亮点 2: the TTT
  * objective is a sum over tokens, so the gradient of any token set is the sum of

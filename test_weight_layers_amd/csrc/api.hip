@@ -14,6 +14,12 @@
 
 using namespace ttt;
 
+// Scratch of ttt_update_noalloc: one copy per device, held by the loaded code object
+// until the process ends.  Host code never uses this name as an address: it takes the
+// device address from hipGetSymbolAddress (scratch_base below).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -56,17 +62,22 @@ hipEvent_t take_event() {
   return e;
 }
 
+// Set for the duration of an allocation-free call: no timing events are created or
+// recorded in it, whatever ttt_profile_enable says.
+thread_local bool t_no_events = false;
+
 template <class F>
 int run(int kind, const char *what, hipStream_t s, F &&f) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (g_prof) {
+  const bool prof = g_prof && !t_no_events;
+  if (prof) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     e0 = take_event();
     e1 = take_event();
     if (e0) hipEventRecord(e0, s);
   }
   const hipError_t err = f();
-  if (g_prof && e0 && e1) {
+  if (prof && e0 && e1) {
     hipEventRecord(e1, s);
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_pending.push_back({kind, e0, e1});
@@ -539,11 +550,65 @@ int ttt_update_ex(int32_t heads, int32_t d, int32_t m, const float *w1, const fl
                    (flags & TTT_NORM_PRESERVE) != 0);
 }
 
+// ------------------------------------------------------- allocation-free update
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept: each device holds its own copy at its own address.
+static int scratch_base(char **out) {
+  static std::mutex mu;
+  static void *base[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TTT_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TTT_EUNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(TTT_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    base[dev] = ptr;
+  }
+  *out = static_cast<char *>(base[dev]);
+  return TTT_OK;
+}
+
+int ttt_update_noalloc(int32_t heads, int32_t d, int32_t m, const float *w1, const float *w3, const float *w2,
+                       float *w1_out, float *w3_out, float *w2_out, const void *k, const void *v, int64_t ld_kv,
+                       const float *eta, int64_t eta_head_stride, int64_t n, float lr, int32_t steps,
+                       int32_t dtype, uint32_t flags, float *grad_out, float *ns_out, void *stream) {
+  int st = check_update_args(heads, d, m, w1, w3, w2, w1_out, w3_out, w2_out, n, lr, steps, dtype, flags);
+  if (st) return st;
+  if ((st = check_token_limits(n, ld_kv, dtype, "k/v"))) return st;
+  if (n > 0) {
+    if ((st = check_rows(k, ld_kv, heads, d, dtype, "k"))) return st;
+    if ((st = check_rows(v, ld_kv, heads, d, dtype, "v"))) return st;
+    if (!eta) return fail(TTT_EINVAL, "eta is null");
+    if (eta_head_stride < 0) return fail(TTT_EINVAL, "eta_head_stride must be >= 0");
+  }
+  const UpdatePlan P = plan_update(heads, d, m, n, dtype);
+  if (P.total > kNoAllocScratchBytes)
+    return fail(TTT_EWORKSPACE, "this update needs %zu bytes of scratch; the allocation-free entry point holds %zu",
+                P.total, kNoAllocScratchBytes);
+  char *ws = nullptr;
+  if ((st = scratch_base(&ws))) return st;
+  t_no_events = true;
+  st = do_update(P, W3{w1, w3, w2}, W3o{w1_out, w3_out, w2_out}, k, v, ld_kv, eta, eta_head_stride, lr, steps,
+                 grad_out, ns_out, ws, static_cast<hipStream_t>(stream), (flags & TTT_NORM_PRESERVE) != 0);
+  t_no_events = false;
+  return st;
+}
+
+int ttt_noalloc_scratch_bytes(size_t *bytes) {
+  if (!bytes) return fail(TTT_EINVAL, "bytes is null");
+  *bytes = kNoAllocScratchBytes;
+  return TTT_OK;
+}
+
 // ------------------------------------------------------- out-of-core update
 // One copy stream per device (default priority, created on first use, kept for
 // the life of the process): host -> device copies of the next batch run on it
 // while the gradient of the current one runs on the caller's stream.
-int copy_stream(hipStream_t *out) {
+static int copy_stream(hipStream_t *out) {
   static std::mutex mu;
   static hipStream_t streams[64] = {};
   int dev = 0;

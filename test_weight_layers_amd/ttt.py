@@ -24,7 +24,7 @@ NORM_PRESERVE = 1
 EXPORTS = ("ttt_last_error", "ttt_update_workspace_bytes", "ttt_apply_workspace_bytes", "ttt_update",
            "ttt_update_ex", "ttt_update_host_workspace_bytes", "ttt_update_host", "ttt_apply", "ttt_output_gate", "ttt_shortconv2d", "ttt_stream_workspace_bytes",
            "ttt_stream", "ttt_stream_ex", "ttt_set_option", "ttt_profile_enable", "ttt_profile_reset",
-           "ttt_profile_read")
+           "ttt_profile_read", "ttt_update_noalloc", "ttt_noalloc_scratch_bytes")
 
 _lib = None
 
@@ -52,6 +52,9 @@ def load() -> ctypes.CDLL:
                                       i32, vp, vp, vp, sz, vp]),
         "ttt_update_ex": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, f32,
                                          i32, i32, u32, vp, vp, vp, sz, vp]),
+        "ttt_update_noalloc": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, f32,
+                                              i32, i32, u32, vp, vp, vp]),
+        "ttt_noalloc_scratch_bytes": (ctypes.c_int, [szp]),
         "ttt_update_host_workspace_bytes": (ctypes.c_int, [i32, i32, i32, i64, i64, i32, szp]),
         "ttt_update_host": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, i64,
                                            f32, i32, i32, u32, vp, vp, vp, sz, vp]),
@@ -204,6 +207,41 @@ def update(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: tor
                                 _ptr(ns_out), _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                 _stream()))
     return tuple(out)
+
+
+def update_noalloc(w: Sequence[torch.Tensor], k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor, lr: float,
+                   steps: int = 1, out: Optional[Sequence[torch.Tensor]] = None,
+                   grad_out: Optional[torch.Tensor] = None, ns_out: Optional[torch.Tensor] = None,
+                   norm_preserve: bool = False):
+    """``update`` through the allocation-free entry point (library-owned scratch, no
+    workspace).  ``out`` must be given by callers that may not allocate."""
+    H, d, m = _weights(w)
+    if out is None:
+        out = tuple(torch.empty_like(x) for x in w)
+    _weights(out)
+    n = k.shape[0]
+    code = _dtype_code(k)
+    if v.dtype != k.dtype or v.shape != k.shape or v.stride() != k.stride():
+        raise ValueError("k and v must share dtype, shape and strides")
+    ld = _rows(k, "k")
+    if k.shape[1] < H * d:
+        raise ValueError(f"k rows must hold H*d = {H * d} columns")
+    ehs = _eta_stride(eta, H, n, k.device)
+    for t, name in ((grad_out, "grad_out"), (ns_out, "ns_out")):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != 3 * H * d * m or not t.is_contiguous()
+                              or t.device != k.device):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of 3*H*m*d elements on k's GPU")
+    flags = NORM_PRESERVE if norm_preserve else 0
+    _check(load().ttt_update_noalloc(H, d, m, *map(_ptr, w), *map(_ptr, out), k.data_ptr(), v.data_ptr(), ld,
+                                     eta.data_ptr(), ehs, n, float(lr), int(steps), code, flags, _ptr(grad_out),
+                                     _ptr(ns_out), _stream()))
+    return tuple(out)
+
+
+def noalloc_scratch_bytes() -> int:
+    out = ctypes.c_size_t()
+    _check(load().ttt_noalloc_scratch_bytes(ctypes.byref(out)))
+    return out.value
 
 
 def update_host_workspace_bytes(heads: int, d: int, m: int, batch: int, ld: int, dtype: torch.dtype) -> int:
