@@ -29,12 +29,16 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c5a")
     ap.add_argument("--frames", type=int, default=0, help="override the workload's frame count")
     ap.add_argument("--cpu-sample-frames", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-only", action="store_true",
+                    help="only time the CPU oracle on the workload (no GPU use); prints one JSON line")
+    ap.add_argument("--oracle-threads", type=int, default=0,
+                    help="limit the oracle's BLAS threads (0 = the library default, all cores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     ap.add_argument("--no-profile-events", action="store_true")
@@ -105,6 +109,24 @@ def gate_flops(cfg, nq):
     return 2.0 * nq * (cfg.heads * cfg.d) ** 2 if cfg.gate else 0.0
 
 
+def per_call_stats(marks):
+    """Median and p90 over the timed steps of each API call's HIP-event time (and of
+    the whole step, from its first to its last mark)."""
+    import numpy as np
+    calls, steps = {}, []
+    first = None
+    for (tag, e), nxt in zip(marks, marks[1:] + [None]):
+        if tag == "start":
+            first = e
+        if nxt is not None and nxt[0] != "start":
+            calls.setdefault(nxt[0], []).append(e.elapsed_time(nxt[1]))
+        if nxt is None or nxt[0] == "start":
+            steps.append(first.elapsed_time(e))
+    calls["step"] = steps
+    return {k: {"median": float(np.median(v)), "p90": float(np.percentile(v, 90)), "n": len(v)}
+            for k, v in calls.items()}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30   # 1 GiB
@@ -118,10 +140,11 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
 
 
-def cpu_baseline(cfg, frames):
-    """Time the fp32 NumPy oracle on `frames` frames of the same workload."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+def cpu_baseline(cfg, frames, threads=0):
+    """Time the fp32 NumPy oracle on `frames` frames of the same workload (BLAS limited
+    to `threads` threads when > 0)."""
+    import contextlib
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from test_weight_layers_amd import synth
@@ -133,6 +156,20 @@ def cpu_baseline(cfg, frames):
     if cfg.conv:
         conv = dict(wconv=f32(inp.wconv), frames=frames, tokens_per_frame=cfg.tokens_per_frame,
                     n_special=cfg.n_special, grid_h=cfg.grid_h, grid_w=cfg.grid_w)
+    limit = threadpool_limits(limits=threads) if threads > 0 else contextlib.nullcontext()
+    with limit:
+        dt, threads_used = _time_oracle(oracle, synth, cfg, args, conv, f32, inp)
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads_used), "kind": "oracle",
+            "sample": f"{frames} frames x {cfg.tokens_per_frame} tokens = {n} tokens of {cfg.name}, "
+                      f"fp32 NumPy oracle, full layer (conv={cfg.conv}, steps={cfg.steps}, apply"
+                      f"{', streamed in chunks' if cfg.chunk_frames else ''}"
+                      f"{', norm-preserving step' if cfg.norm_preserve else ''}"
+                      f"{', gated output' if cfg.gate else ''}), "
+                      f"{dt:.2f} s wall"}
+
+
+def _time_oracle(oracle, synth, cfg, args, conv, f32, inp):
+    from threadpoolctl import threadpool_info
     t0 = time.perf_counter()
     if cfg.chunk_frames:
         oracle.stream(*args, cfg.lr, cfg.steps, chunk=cfg.chunk_frames * cfg.tokens_per_frame,
@@ -147,13 +184,29 @@ def cpu_baseline(cfg, frames):
             oracle.output_gate(o, f32(wg), f32(gamma), cfg.gate_eps)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{frames} frames x {cfg.tokens_per_frame} tokens = {n} tokens of {cfg.name}, "
-                      f"fp32 NumPy oracle, full layer (conv={cfg.conv}, steps={cfg.steps}, apply"
-                      f"{', streamed in chunks' if cfg.chunk_frames else ''}"
-                      f"{', norm-preserving step' if cfg.norm_preserve else ''}"
-                      f"{', gated output' if cfg.gate else ''}), "
-                      f"{dt:.2f} s wall"}
+    return dt, threads
+
+
+def timed_median(fn, reps, warmup, min_warm_s=0.2):
+    """Median seconds of `reps` calls of fn, each bracketed by HIP events on the current
+    stream, after at least `warmup` calls and `min_warm_s` seconds of warm-up."""
+    import numpy as np
+    import torch
+    t_end = time.perf_counter() + min_warm_s
+    i = 0
+    while i < warmup or time.perf_counter() < t_end:
+        fn()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
 
 
 def linear_sweep(steps, warmup):
@@ -191,22 +244,11 @@ def linear_sweep(steps, warmup):
             ttt.update(w0, k, v, eta, cfg.lr, 1, out=w_out, workspace=ws_u)
             ttt.apply(w_out, q, out=o, workspace=ws_a)
 
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        rows.append((n, (time.perf_counter() - t0) / steps))
-        for _ in range(warmup):
-            ttt.apply(w_out, q_fix, out=o_fix, workspace=ws_f)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            ttt.apply(w_out, q_fix, out=o_fix, workspace=ws_f)
-        torch.cuda.synchronize()
-        fixed.append((time.perf_counter() - t0) / steps)
+        # Each size is timed with the GPU at its working clock: warm-up calls fill at least
+        # 200 ms of GPU time, then every timed call is bracketed by HIP events on the
+        # launch stream and the median is kept (clock ramps and one-off stalls fall out).
+        rows.append((n, timed_median(step, steps, warmup)))
+        fixed.append(timed_median(lambda: ttt.apply(w_out, q_fix, out=o_fix, workspace=ws_f), steps, warmup))
         print(json.dumps({"sweep_frames": f, "tokens": n, "ms": rows[-1][1] * 1e3,
                           "apply_fixed_ms": fixed[-1] * 1e3}), flush=True)
     ns = np.array([r[0] for r in rows], float)
@@ -216,7 +258,8 @@ def linear_sweep(steps, warmup):
     fit = t0 + beta * ns
     r2 = 1.0 - np.sum((ts - fit) ** 2) / np.sum((ts - ts.mean()) ** 2)
     i1000 = frames.index(1000)
-    out = {"sweep": "zipmap-shape 4x256/512, update (1 step) + apply on the same N tokens",
+    out = {"sweep": "zipmap-shape 4x256/512, update (1 step) + apply on the same N tokens; median of "
+                    f"{steps} event-timed calls per size after >= 200 ms of warm-up",
            "frames": frames, "tokens": ns.tolist(), "seconds": ts.tolist(), "t0_s": t0,
            "beta_s_per_token": beta, "r2": r2, "max_rel_residual": float(np.max(np.abs(ts - fit) / ts)),
            "t0_over_t_at_1000_frames": float(t0 / ts[i1000]),
@@ -271,6 +314,13 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding "
               "is a design note, not built.", file=sys.stderr)
         sys.exit(2)
+    if args.oracle_only:
+        from test_weight_layers_amd.configs import CONFIGS
+        cfg = CONFIGS[args.config]
+        frames = min(args.cpu_sample_frames, args.frames or cfg.frames)
+        print(json.dumps({"workload": cfg.name, "cpu_baseline": cpu_baseline(cfg, frames, args.oracle_threads)}),
+              flush=True)
+        return
     import torch
     if args.copy_calibration:
         copy_calibration()
@@ -301,6 +351,16 @@ def main():
     w_out = tuple(torch.empty_like(x) for x in w0)
     o = torch.empty((nq, H * d), dtype=dt, device="cuda")
     chunk = cfg.chunk_frames * cfg.tokens_per_frame
+    # per-call HIP events on the launch stream (torch's current stream, which the
+    # library launches on), recorded between the API calls of each timed step
+    marks, recording = [], [False]
+
+    def mark(tag):
+        if recording[0]:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.append((tag, e))
+
     if chunk:
         # causal stream: per chunk apply with the current W, then update W from the chunk
         ws = torch.empty(ttt.stream_workspace_bytes(H, d, m, chunk, dt), dtype=torch.uint8, device="cuda")
@@ -308,8 +368,10 @@ def main():
         def step():
             for a, b in zip(w_out, w0):
                 a.copy_(b)
+            mark("start")
             ttt.stream(w_out, inp.k, inp.v, inp.eta, inp.q, cfg.lr, cfg.steps, chunk, out=o, workspace=ws,
                        norm_preserve=cfg.norm_preserve)
+            mark("stream")
     else:
         v2 = torch.empty_like(inp.v)
         ws_u = torch.empty(ttt.update_workspace_bytes(H, d, m, n, dt), dtype=torch.uint8, device="cuda")
@@ -321,18 +383,25 @@ def main():
 
         def step():
             v = inp.v
+            mark("start")
             if cfg.conv:
                 ttt.shortconv2d(inp.v, inp.wconv, **geo, out=v2)
                 v = v2
+                mark("conv")
             ttt.update(w0, inp.k, v, inp.eta, cfg.lr, cfg.steps, out=w_out, workspace=ws_u,
                        norm_preserve=cfg.norm_preserve)
+            mark("update")
             ttt.apply(w_out, inp.q, out=o, workspace=ws_a)
+            mark("apply")
             if cfg.gate:
                 ttt.output_gate(o, wg, gamma, cfg.gate_eps, out=o_gated)
+                mark("gate")
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    marks.clear()
+    recording[0] = True
     prof = not args.no_profile_events
     ttt.profile_reset()
     ttt.profile_enable(prof)
@@ -342,6 +411,7 @@ def main():
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    recording[0] = False
     ttt.profile_enable(False)
     kt = ttt.profile_read() if prof else {}
     ms_step = elapsed * 1e3 / args.steps
@@ -403,8 +473,10 @@ def main():
             conv_bytes = 2.0 * n * H * d * inp.v.element_size()
             out["conv_kernel"] = {"achieved_gbs": conv_bytes / c_avg / 1e9, "peak_gbs": PEAK_HBM_GBS,
                                   "frac": conv_bytes / c_avg / 1e9 / PEAK_HBM_GBS, "avg_launch_ms": c_avg * 1e3}
+    if marks:
+        out["per_call_ms"] = per_call_stats(marks)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample_frames, cfg.frames))
+        out["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample_frames, cfg.frames), args.oracle_threads)
     print(json.dumps(out), flush=True)
 
 

@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/ttt.h"
+#include "ttt.h"
 #include "kernels.h"
 
 using namespace ttt;
