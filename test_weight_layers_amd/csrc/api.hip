@@ -158,13 +158,23 @@ UpdatePlan plan_update(int H, int d, int m, int64_t n, int dtype) {
   p.splits = (int)s;
   p.grid = (int)(per_split * s);
   if (p.big) {
-    // wide heads: the contraction kernels split the tokens; about 512 workgroups
-    // for the smaller of the two contraction launches
+    // Wide heads: the two contraction kernels split the tokens into S ranges, each
+    // writing a full fp32 partial of G (3 H d m floats) that the optimiser step sums.
+    // More ranges fill more CUs but add partial traffic; S minimises a simple cost:
+    // the launches' rounds of 256 workgroups times one workgroup's blocks (~1 us per
+    // 32-token block), plus writing and reading the partials at ~4 TB/s.
     p.n_pad = big_pad_tokens(n);
-    const int64_t tiles = (int64_t)H * big_contract_tiles(d, m, 1);
-    int64_t sb = (512 + tiles - 1) / tiles;
-    if (g_splits > 0) sb = g_splits;
     const int64_t blocks = p.n_pad / 32;
+    const int64_t t0 = (int64_t)H * big_contract_tiles(d, m, 0), t1 = (int64_t)H * big_contract_tiles(d, m, 1);
+    const double part_bytes = 3.0 * H * d * m * 4.0;
+    int64_t sb = 1;
+    double best = 0.0;
+    for (int64_t sc = 1; sc <= 64 && sc <= (blocks > 0 ? blocks : 1); ++sc) {
+      const int64_t rounds = (t0 * sc + 255) / 256 + (t1 * sc + 255) / 256;
+      const double cost = (double)rounds * (double)((blocks + sc - 1) / sc) * 1000.0 + 2.0 * sc * part_bytes / 4000.0;
+      if (sc == 1 || cost < best) best = cost, sb = sc;
+    }
+    if (g_splits > 0) sb = g_splits;
     if (blocks > 0 && sb > blocks) sb = blocks;
     p.splits = (int)(sb < 1 ? 1 : sb);
     p.grid = 0;

@@ -430,9 +430,27 @@ __global__ __launch_bounds__(256) void ns_tile_kernel(NsStepParams p, int cur, i
   const int H = p.heads, d = p.d, m = p.m, r = p.r, c = p.c;
   const int64_t mat = (int64_t)d * m, srr = (int64_t)r * r;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
-  const int rt = r / kT, nt = PH < 2 ? rt : c / kT;        // output tiles per matrix: rt x nt
+  // A = X X^T and B = b A + c A A are symmetric: PH 0 and 1 compute the upper-triangle
+  // tiles (ti <= tj) only and write each off-diagonal one mirrored as well.  PH 2 and 3
+  // cover all rt x (c / kT) tiles of X'.
+  const int rt = r / kT, nt = PH < 2 ? rt : c / kT;
+  const int per_mat = PH < 2 ? rt * (rt + 1) / 2 : rt * nt;
   const int tile = xcd_item();
-  const int b = tile / (rt * nt), ti = (tile / nt) % rt, tj = tile % nt;
+  const int b = tile / per_mat;
+  int ti, tj;
+  if (PH < 2) {
+    int k = tile % per_mat;
+    ti = 0;
+    while (k >= rt - ti) {
+      k -= rt - ti;
+      ++ti;
+    }
+    tj = ti + k;
+  } else {
+    ti = (tile % per_mat) / nt;
+    tj = tile % nt;
+  }
+  const bool mirror = PH < 2 && ti != tj;
   const float *X = p.x[cur] + (int64_t)b * mat, *XT = p.xt[cur] + (int64_t)b * mat;
   const float *A = p.am + b * srr;
   float *Bm = p.bm + b * srr;
@@ -462,14 +480,22 @@ __global__ __launch_bounds__(256) void ns_tile_kernel(NsStepParams p, int cur, i
     for (int e = 0; e < 2; ++e) {
       const int i = ti * kT + (w >> 1) * 32 + 16 * a + 4 * g, jj = tj * kT + (w & 1) * 32 + 16 * e + li;
       if (PH == 0) {
+        f32x4 v;
 #pragma unroll
-        for (int z = 0; z < 4; ++z) p.am[b * srr + (int64_t)(i + z) * r + jj] = alpha * acc[a][e][z];
+        for (int z = 0; z < 4; ++z) {
+          v[z] = alpha * acc[a][e][z];
+          p.am[b * srr + (int64_t)(i + z) * r + jj] = v[z];
+        }
+        if (mirror) *reinterpret_cast<f32x4 *>(p.am + b * srr + (int64_t)jj * r + i) = v;
       } else if (PH == 1) {
+        f32x4 v;
 #pragma unroll
         for (int z = 0; z < 4; ++z) {
           const int64_t o = (int64_t)(i + z) * r + jj;
-          Bm[o] = p.c_coef * acc[a][e][z] + p.b_coef * A[o];
+          v[z] = p.c_coef * acc[a][e][z] + p.b_coef * A[o];
+          Bm[o] = v[z];
         }
+        if (mirror) *reinterpret_cast<f32x4 *>(Bm + (int64_t)jj * r + i) = v;
       } else {
         // X[i .. i+3][jj] is the contiguous X^T[jj][i .. i+3]
         const f32x4 xo = *reinterpret_cast<const f32x4 *>(XT + (int64_t)jj * r + i);
@@ -608,8 +634,9 @@ hipError_t ns_optimiser_impl(const NsStepParams &p, hipStream_t s) {
   int cur = 0;
   for (int it = 0; it < p.iters; ++it) {
     const int first = it == 0;
-    hipLaunchKernelGGL((ns_tile_kernel<T, 0>), dim3(B * rt * rt), dim3(256), 0, s, p, cur, first);
-    hipLaunchKernelGGL((ns_tile_kernel<T, 1>), dim3(B * rt * rt), dim3(256), 0, s, p, cur, first);
+    const int tri = B * rt * (rt + 1) / 2;      // upper-triangle tiles of the symmetric products
+    hipLaunchKernelGGL((ns_tile_kernel<T, 0>), dim3(tri), dim3(256), 0, s, p, cur, first);
+    hipLaunchKernelGGL((ns_tile_kernel<T, 1>), dim3(tri), dim3(256), 0, s, p, cur, first);
     if (it + 1 < p.iters)
       hipLaunchKernelGGL((ns_tile_kernel<T, 2>), dim3(B * rt * ct), dim3(256), 0, s, p, cur, first);
     else
