@@ -107,23 +107,32 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
   auto compute = [&](const unsigned char *base) {
     // Z^T rows = hidden perm_row(u, li) of the chunk, cols = tokens
     f32x4 z1[2][2], z3[2][2];
+    // (u, kc) steps; the W1 / W3 fragment reads run two steps ahead of their MFMAs
+    constexpr int NQ = 2 * KC, RA = 3;
+    bf16x8 ra1[RA], ra3[RA];
+    auto rd = [&](int q, int slot) __attribute__((always_inline)) {
+      int ba = base_a[q / KC];              // one XOR per read rather than held addresses
+      asm volatile("" : "+v"(ba));
+      const unsigned char *pa = base + (ba ^ (64 * (q % KC)));
+      ra1[slot] = *reinterpret_cast<const bf16x8 *>(pa);
+      ra3[slot] = *reinterpret_cast<const bf16x8 *>(pa + L::kTile);
+    };
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < 2; ++t) z1[u][t] = z3[u][t] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        int ba = base_a[u];                 // one XOR per read rather than held addresses
-        asm volatile("" : "+v"(ba));
-        const unsigned char *pa = base + (ba ^ (64 * kc));
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(pa);
-        const bf16x8 a3 = *reinterpret_cast<const bf16x8 *>(pa + L::kTile);
+    for (int q = 0; q < RA - 1; ++q) rd(q, q);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          z1[u][t] = mma(a1, qf[t][kc], z1[u][t]);
-          z3[u][t] = mma(a3, qf[t][kc], z3[u][t]);
-        }
+    for (int q = 0; q < NQ; ++q) {
+      if (q + RA - 1 < NQ) rd(q + RA - 1, (q + RA - 1) % RA);
+      const int u = q / KC, kc = q % KC, sl = q % RA;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        z1[u][t] = mma(ra1[sl], qf[t][kc], z1[u][t]);
+        z3[u][t] = mma(ra3[sl], qf[t][kc], z3[u][t]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // H = SiLU(z1) o z3; element v = 4u + r is hidden 8g + v of the chunk
     bf16x8 hf[2];

@@ -182,6 +182,23 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
     if (NST > 3 && kc + 3 < nk) step(kc + 3, st3, st2);
   }
 
+  // The epilogue's O' loads (16 rows of 8 channels per thread, rows past n read row
+  // n - 1) are issued first, so that their latency overlaps the RMS and SiLU work.
+  bf16x8 xs[16];
+  f32x4 g0 = f32x4{0, 0, 0, 0}, g1 = g0;
+  if constexpr (sizeof(T) == 2) {
+    const int ch = j0 + 8 * (t & 31);
+    if (ch < C) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int64_t tok = tok0 + 16 * i + (t >> 5);
+        if (tok >= p.n) tok = p.n - 1;
+        xs[i] = *reinterpret_cast<const bf16x8 *>(oin + tok * p.ld_in + ch);
+      }
+      g0 = *reinterpret_cast<const f32x4 *>(p.gamma + ch);
+      g1 = *reinterpret_cast<const f32x4 *>(p.gamma + ch + 4);
+    }
+  }
   // row sums of squares: lanes li, li+16, li+32, li+48 of a channel-0 wave hold
   // the four element groups of row 64 wr + 16 a + li
   if (wc == 0) {
@@ -224,16 +241,6 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
     const int cv = t & 31;                      // 8-channel group of the tile
     const int ch = j0 + 8 * cv;
     if (ch >= C) return;
-    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(p.gamma + ch);
-    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(p.gamma + ch + 4);
-    // all 16 rows' O' loads in flight at once (rows past n read row n - 1)
-    bf16x8 xs[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int64_t tok = tok0 + 16 * i + (t >> 5);
-      if (tok >= p.n) tok = p.n - 1;
-      xs[i] = *reinterpret_cast<const bf16x8 *>(oin + tok * p.ld_in + ch);
-    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = 16 * i + (t >> 5);

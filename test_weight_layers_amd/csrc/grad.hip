@@ -123,6 +123,15 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
   // The rates of a block come with it (wave 4, one dword per lane) through a
   // range-checked buffer view that ends at token n: rates past n arrive as 0.
   const float *eta = p.eta + (int64_t)h * p.eta_hs;
+  // Per-lane byte offset of each piece's rows inside a block: the same for every block,
+  // so it is formed once and held (rebuilding it per block costs the copying waves
+  // about 30 VALU instructions per block, measurably more than the two registers).
+  unsigned soff[PPW];
+#pragma unroll
+  for (int q = 0; q < PPW; ++q) {
+    const int r = kRowsPer * (c * PPW + q) + l / L::kChunks;
+    soff[q] = (unsigned)r * row_bytes + 16u * (unsigned)((l % L::kChunks) ^ (swz_kv(r) & (L::kChunks - 1)));
+  }
   auto stage_block = [&](int blk, unsigned char *dst) {
     if (forward_role || c >= NDMA) return;
     const int t0 = blk * kTokBlock;
@@ -132,18 +141,7 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
       __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void *)(dst + L::kEta), 4,
                                                4u * (unsigned)l, 0, 0, 0);
     }
-    // Per-lane byte offset of each piece's rows inside a block, rebuilt here from the
-    // lane index (a few VALU operations) rather than held in registers across the
-    // loop: the empty asm keeps the compiler from hoisting them out of it.
-    int lane = l;
-    asm volatile("" : "+v"(lane));
-    auto piece_row = [&](int q) { return kRowsPer * (c * PPW + q) + lane / L::kChunks; };
-    unsigned soff[PPW];
-#pragma unroll
-    for (int q = 0; q < PPW; ++q) {
-      const int r = piece_row(q);
-      soff[q] = (unsigned)r * row_bytes + 16u * (unsigned)((lane % L::kChunks) ^ (swz_kv(r) & (L::kChunks - 1)));
-    }
+    auto piece_row = [&](int q) { return kRowsPer * (c * PPW + q) + l / L::kChunks; };
     // wave-uniform buffer views of the block's 32 rows; unsigned per-lane offsets
     const __amdgpu_buffer_rsrc_t kr = buffer_view(Kh + (int64_t)t0 * p.ld, kTokBlock * row_bytes);
     const __amdgpu_buffer_rsrc_t vr = buffer_view(Vh + (int64_t)t0 * p.ld, kTokBlock * row_bytes);
