@@ -111,9 +111,8 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
     constexpr int NQ = 2 * KC, RA = 3;
     bf16x8 ra1[RA], ra3[RA];
     auto rd = [&](int q, int slot) __attribute__((always_inline)) {
-      int ba = base_a[q / KC];              // one XOR per read rather than held addresses
-      asm volatile("" : "+v"(ba));
-      const unsigned char *pa = base + (ba ^ (64 * (q % KC)));
+      // one XOR per read rather than held addresses
+      const unsigned char *pa = base + xor_here(base_a[q / KC], 64 * (q % KC));
       ra1[slot] = *reinterpret_cast<const bf16x8 *>(pa);
       ra3[slot] = *reinterpret_cast<const bf16x8 *>(pa + L::kTile);
     };
@@ -154,10 +153,8 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
     constexpr int kRing = 8;
     bf16x4 wlo[kRing], whi[kRing];
     auto rd_w2 = [&](int dt) __attribute__((always_inline)) {
-      int b0 = base_b[0], b1 = base_b[1];
-      asm volatile("" : "+v"(b0), "+v"(b1));
-      wlo[dt % kRing] = lds_read_tr16(base + (b0 ^ (32 * dt)));
-      whi[dt % kRing] = lds_read_tr16(base + (b1 ^ (32 * dt)));
+      wlo[dt % kRing] = lds_read_tr16(base + xor_here(base_b[0], 32 * dt));
+      whi[dt % kRing] = lds_read_tr16(base + xor_here(base_b[1], 32 * dt));
     };
 #pragma unroll
     for (int q = 0; q < kRing - 1 && q < DT; ++q) rd_w2(q);

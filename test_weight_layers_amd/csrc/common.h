@@ -161,6 +161,16 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// base ^ k formed by one VALU instruction at this point of the program: the compiler
+// can neither hoist it out of a loop (holding one register per k) nor needs to copy
+// the base first (as an empty asm that modifies a copy of the base would).
+__device__ __forceinline__ int xor_here(int base, int k) {
+  if (k == 0) return base;
+  int r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(k), "v"(base));
+  return r;
+}
+
 __device__ __forceinline__ bf16x8 cat8(const bf16x4 a, const bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }

@@ -236,13 +236,9 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
       auto lda = [&](int kc, int slot) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          // V's address passes through an empty asm: otherwise the K and V reads
-          // (16 KB apart) merge into paired reads whose results need register moves
-          int v0 = base_a[u] ^ (64 * kc);
-          const unsigned char *p0 = cur + v0;
-          asm volatile("" : "+v"(v0));
-          kf[slot][u] = *reinterpret_cast<const bf16x8 *>(p0);
-          vf[slot][u] = *reinterpret_cast<const bf16x8 *>(cur + L::kTile + v0);
+          const int a = xor_here(base_a[u], 64 * kc);
+          kf[slot][u] = *reinterpret_cast<const bf16x8 *>(cur + a);
+          vf[slot][u] = *reinterpret_cast<const bf16x8 *>(cur + L::kTile + a);
         }
       };
 #pragma unroll
@@ -320,12 +316,10 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     auto contract_block = [&](const unsigned char *blk, const bf16x8 pk1, const bf16x8 pk3, const bf16x8 pkh) {
       bf16x8 ktf[2], vtf[2];
       auto ldb = [&](int dt, int slot) {
-        // the bases pass through an empty asm so that each address is formed (one
-        // XOR) right before its read instead of 32 of them being held in registers
-        int b0 = base_b[0], b1 = base_b[1];
-        asm volatile("" : "+v"(b0), "+v"(b1));
-        const unsigned char *p0 = blk + (b0 ^ (32 * dt));
-        const unsigned char *p1 = blk + (b1 ^ (32 * dt));
+        // each address is formed (one XOR) right before its read instead of 32 of them
+        // being held in registers
+        const unsigned char *p0 = blk + xor_here(base_b[0], 32 * dt);
+        const unsigned char *p1 = blk + xor_here(base_b[1], 32 * dt);
         ktf[slot] = cat8(lds_read_tr16(p0), lds_read_tr16(p1));
         vtf[slot] = cat8(lds_read_tr16(p0 + L::kTile), lds_read_tr16(p1 + L::kTile));
       };
