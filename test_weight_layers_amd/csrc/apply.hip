@@ -62,20 +62,20 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i][0] = acc[i][1] = f32x4{0, 0, 0, 0};
 
-  // DMA: piece b of a stage is tile b / PPT, rows kRowsPer * (b % PPT) ..; lane l
-  // fills row r at physical chunk l % kChunks = logical chunk ^ swizzle(tile, r).
+  // DMA: piece b of a stage is tile b / PPT (W1, W3, W2^T), rows kRowsPer * (b % PPT)
+  // + lr with lr = lane / kChunks; lane l fills row r at physical chunk l % kChunks,
+  // which holds the logical chunk (l % kChunks) ^ swizzle(tile, r).  Both swizzles
+  // copy row bits onto chunk bits one by one, so swizzle(kRowsPer p + lr) =
+  // swizzle(kRowsPer p) ^ swizzle(lr): a lane's source offset is its own constant
+  // (held, one per swizzle) XORed with a wave-uniform one, plus 1 KB per piece.
+  auto lane_part = [&](bool b128) {
+    const int lr = l / L::kChunks;
+    const int sw = (b128 ? swz_rows_b128(lr) : swz_rows(lr)) & (L::kChunks - 1);
+    return (unsigned)(lr * L::kRowBytes + 16 * ((l % L::kChunks) ^ sw));
+  };
+  const unsigned lane_b128 = lane_part(true), lane_rows = lane_part(false);
   const char *wsrc[3] = {static_cast<const char *>(p.w1), static_cast<const char *>(p.w3),
                          static_cast<const char *>(p.w2t)};
-  // offset of piece q in a chunk, formed at each use (the lane index passes through
-  // an empty asm) rather than held in registers
-  auto piece_off = [&](int q) {
-    int lw = l;
-    asm volatile("" : "+v"(lw));
-    const int piece = w * PPW + q, mat = piece < NPIECE ? piece / PPT : 0;
-    const int r = kRowsPer * (piece % PPT) + lw / L::kChunks;
-    const int sw = (mat < 2 ? swz_rows_b128(r) : swz_rows(r)) & (L::kChunks - 1);
-    return (r * D + 8 * ((lw % L::kChunks) ^ sw)) * 2;
-  };
   const int64_t head_off = (int64_t)h * p.m * D * 2;
   auto stage_chunk = [&](int hc, unsigned char *dst) {
     const int64_t base = head_off + (int64_t)hc * kHidChunk * D * 2;   // wave-uniform
@@ -83,7 +83,12 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
     for (int q = 0; q < PPW; ++q) {
       const int piece = w * PPW + q;
       if (NPIECE % WV != 0 && piece >= NPIECE) break;     // wave-uniform
-      copy16_to_lds(wsrc[piece / PPT] + base + piece_off(q), dst + piece * 1024);
+      const int mat = piece / PPT, pr = piece % PPT;
+      const int r0 = kRowsPer * pr;
+      const unsigned s = 16u * (unsigned)((mat < 2 ? swz_rows_b128(r0) : swz_rows(r0)) & (L::kChunks - 1));
+      const __amdgpu_buffer_rsrc_t rs = buffer_view(wsrc[mat] + base, L::kTile);
+      copy16_to_lds(rs, xor_scalar_here(mat < 2 ? lane_b128 : lane_rows, s), 1024u * (unsigned)pr,
+                    dst + piece * 1024);
     }
   };
 

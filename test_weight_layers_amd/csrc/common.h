@@ -138,6 +138,18 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, unsig
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(lds_wave_base), 16,
                                            voffset, 0, 0, 0);
 }
+// The same copy with a wave-uniform byte offset `soffset` added to every lane's.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, unsigned soffset,
+                                              unsigned char *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(lds_wave_base), 16,
+                                           voffset, soffset, 0, 0);
+}
+// base ^ k for a wave-uniform k, formed by one VALU instruction at this point.
+__device__ __forceinline__ unsigned xor_scalar_here(unsigned base, unsigned k) {
+  unsigned r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(k), "v"(base));
+  return r;
+}
 // Raw buffer view of `bytes` bytes at `base` (32-bit dword format word of gfx9).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);

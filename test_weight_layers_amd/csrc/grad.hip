@@ -233,12 +233,14 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     auto forward_block = [&](const unsigned char *cur, unsigned char *pkw) {
       f32x4 z1[2], z3[2], pp[2];
       bf16x8 kf[FR][2], vf[FR][2];
+      // the u = 1 rows are the u = 0 rows + 4 (perm_row), which swz_kv ignores (it uses
+      // row bits 0, 1 and 3): one address per reduction chunk, the rest immediate offsets
       auto lda = [&](int kc, int slot) {
+        const unsigned char *pa = cur + xor_here(base_a[0], 64 * kc);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int a = xor_here(base_a[u], 64 * kc);
-          kf[slot][u] = *reinterpret_cast<const bf16x8 *>(cur + a);
-          vf[slot][u] = *reinterpret_cast<const bf16x8 *>(cur + L::kTile + a);
+          kf[slot][u] = *reinterpret_cast<const bf16x8 *>(pa + u * 4 * L::kRowBytes);
+          vf[slot][u] = *reinterpret_cast<const bf16x8 *>(pa + L::kTile + u * 4 * L::kRowBytes);
         }
       };
 #pragma unroll
@@ -318,8 +320,9 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
       auto ldb = [&](int dt, int slot) {
         // each address is formed (one XOR) right before its read instead of 32 of them
         // being held in registers
+        // the q = 1 rows are the q = 0 rows + 4, which swz_kv ignores
         const unsigned char *p0 = blk + xor_here(base_b[0], 32 * dt);
-        const unsigned char *p1 = blk + xor_here(base_b[1], 32 * dt);
+        const unsigned char *p1 = p0 + 4 * L::kRowBytes;
         ktf[slot] = cat8(lds_read_tr16(p0), lds_read_tr16(p1));
         vtf[slot] = cat8(lds_read_tr16(p0 + L::kTile), lds_read_tr16(p1 + L::kTile));
       };
