@@ -824,6 +824,9 @@ int ttt_output_gate(int32_t channels, const void *o_in, int64_t ld_in, const voi
   if (!gamma || reinterpret_cast<uintptr_t>(gamma) % 16 != 0)
     return fail(TTT_EINVAL, "gamma is null or not 16-byte aligned");
   const size_t es = esize(dtype);
+  // the kernel addresses a 256-row tile of o_in and of W_g through 32-bit offsets
+  if ((uint64_t)256 * ld_in * es >= (1ull << 32) || (uint64_t)256 * channels * es >= (1ull << 32))
+    return fail(TTT_EUNSUPPORTED, "256 rows of o_in or W_g must span < 4 GiB");
   const size_t in_b = (size_t)n * ld_in * es, out_b = (size_t)n * ld_out * es, wg_b = (size_t)channels * channels * es;
   if (overlap(o_in, in_b, o_out, out_b)) return fail(TTT_EINVAL, "o_in and o_out must not overlap");
   if (overlap(wg, wg_b, o_out, out_b)) return fail(TTT_EINVAL, "wg and o_out must not overlap");

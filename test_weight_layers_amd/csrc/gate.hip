@@ -60,17 +60,21 @@ template <> __device__ __forceinline__ f32x8 gate_frag<float>(const unsigned cha
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ float frag_sumsq(const bf16x8 v) {
-  float s = 0.0f;
+// sum of squares of 8 bf16 values with four bf16 dot2 instructions (x0^2 + x1^2 + acc,
+// exact products, fp32 sums) instead of eight conversions and eight FMAs
+__device__ __forceinline__ float frag_sumsq(const bf16x8 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s += (float)v[i] * (float)v[i];
-  return s;
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
+  }
+  return acc;
 }
-__device__ __forceinline__ float frag_sumsq(const f32x8 v) {
-  float s = 0.0f;
+__device__ __forceinline__ float frag_sumsq(const f32x8 v, float acc) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s += v[i] * v[i];
-  return s;
+  for (int i = 0; i < 8; ++i) acc += v[i] * v[i];
+  return acc;
 }
 
 
@@ -105,29 +109,32 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
   // DMA sources.  1 KB piece b of a stage's A part holds rows kRowsPerKb * b ..
   // (wave w fills b = kDmaA w ..), of its B part likewise; lane l writes row
   // kRowsPerKb b + l / kPieces at position l % kPieces, which holds the row's
-  // piece (l % kPieces) ^ swizzle.
-  const char *asrc[G::kDmaA];
-  const char *bsrc[G::kDmaB];
+  // piece (l % kPieces) ^ swizzle.  Each lane's source offset inside the tile's rows
+  // is fixed (rows past n read row n - 1, channels past C channel C - 1); the chunk
+  // advances by a wave-uniform offset, so a copy needs no address arithmetic.
+  const int64_t a_rows = p.n - tok0 < kGateTok ? p.n - tok0 : kGateTok;
+  const __amdgpu_buffer_rsrc_t arsrc = buffer_view(oin + tok0 * p.ld_in, (unsigned)(a_rows * p.ld_in * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t brsrc = buffer_view(wg + (int64_t)j0 * C,
+                                                   (unsigned)((C - j0 < kGateCh ? C - j0 : kGateCh) * C * sizeof(T)));
+  unsigned aoff[G::kDmaA], boff[G::kDmaB];
 #pragma unroll
   for (int j = 0; j < G::kDmaA; ++j) {
     const int r = G::kRowsPerKb * (G::kDmaA * w + j) + l / G::kPieces;
-    int64_t tok = tok0 + r;
-    if (tok >= p.n) tok = p.n - 1;
-    asrc[j] = reinterpret_cast<const char *>(oin + tok * p.ld_in) + 16 * ((l % G::kPieces) ^ gate_swz<T>(r));
+    const int rr = r < a_rows ? r : (int)a_rows - 1;
+    aoff[j] = (unsigned)((int64_t)rr * p.ld_in * sizeof(T)) + 16u * (unsigned)((l % G::kPieces) ^ gate_swz<T>(r));
   }
 #pragma unroll
   for (int j = 0; j < G::kDmaB; ++j) {
     const int r = G::kRowsPerKb * (G::kDmaB * w + j) + l / G::kPieces;
-    int ch = j0 + r;
-    if (ch >= C) ch = C - 1;
-    bsrc[j] = reinterpret_cast<const char *>(wg + (int64_t)ch * C) + 16 * ((l % G::kPieces) ^ gate_swz<T>(r));
+    const int rr = j0 + r < C ? r : C - 1 - j0;
+    boff[j] = (unsigned)((int64_t)rr * C * sizeof(T)) + 16u * (unsigned)((l % G::kPieces) ^ gate_swz<T>(r));
   }
   auto issue = [&](int kc, unsigned char *dst) __attribute__((always_inline)) {
-    const int64_t kb = (int64_t)kc * G::kRowB;
+    const unsigned kb = (unsigned)kc * G::kRowB;
 #pragma unroll
-    for (int j = 0; j < G::kDmaA; ++j) copy16_to_lds(asrc[j] + kb, dst + (G::kDmaA * w + j) * 1024);
+    for (int j = 0; j < G::kDmaA; ++j) copy16_to_lds(arsrc, aoff[j], kb, dst + (G::kDmaA * w + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < G::kDmaB; ++j) copy16_to_lds(bsrc[j] + kb, dst + G::kStageA + (G::kDmaB * w + j) * 1024);
+    for (int j = 0; j < G::kDmaB; ++j) copy16_to_lds(brsrc, boff[j], kb, dst + G::kStageA + (G::kDmaB * w + j) * 1024);
   };
 
   f32x4 acc[4][8];
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
       }
       if (wc == 0) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) ss[a] += frag_sumsq(fa[a]);
+        for (int a = 0; a < 4; ++a) ss[a] = frag_sumsq(fa[a], ss[a]);
       }
     }
   };
