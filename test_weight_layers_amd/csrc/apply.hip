@@ -20,9 +20,11 @@ constexpr int kApplyWaves = 8;   // waves (of 32 tokens) per fast workgroup
 // waves, two per SIMD when WV = 8); each wave keeps its Q fragments and its O^T
 // accumulators in registers.  The head's weights stream through LDS 32 hidden
 // units at a time: W1 and W3 rows and W2^T rows ([hidden][d], so the second
-// product reads them with the transposing load), DMA'd into one of two separate
-// stage arrays while the other is consumed.  Every weight byte fetched serves
-// 32 WV tokens, so the tile is as tall as the register file allows.
+// product reads them with the transposing load), DMA'd into a ring of three
+// separate stage arrays.  Every weight byte fetched serves 32 WV tokens, so the
+// tile is as tall as the register file allows.  The chunks run as a software
+// pipeline (see the loop) so that each wave's SiLU-gate VALU work issues between
+// its own MFMAs, and O leaves through LDS as whole rows.
 template <int D>
 struct ApplyLayout {
   static constexpr int kChunks = D / 8;
@@ -37,8 +39,10 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
   constexpr int KC = D / 32, DT = D / 16;
   constexpr int NPIECE = L::kStage / 1024, PPW = (NPIECE + WV - 1) / WV, kRowsPer = 1024 / L::kRowBytes;
   constexpr int PPT = NPIECE / 3;                        // 1 KB pieces per tile
+  static_assert(WV <= 9, "the O staging puts three waves' rows in each stage array");
   __shared__ __attribute__((aligned(16))) unsigned char sa[L::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char sb[L::kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char sc[L::kStage];
 
   const int h = blockIdx.x % p.heads;
   const int64_t tile = blockIdx.x / p.heads;
@@ -109,53 +113,54 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
                 8 * (li & 1);
   }
 
-  auto compute = [&](const unsigned char *base) {
-    // Z^T rows = hidden perm_row(u, li) of the chunk, cols = tokens
-    f32x4 z1[2][2], z3[2][2];
-    // (u, kc) steps; the W1 / W3 fragment reads run two steps ahead of their MFMAs
-    constexpr int NQ = 2 * KC, RA = 3;
+  // First product for hidden half u (tile rows perm_row(u, .)) of the chunk staged at
+  // `base`: z1, z3 for the two token tiles, over d in KC steps; the W1 / W3 fragment
+  // reads run one step ahead (a deeper ring does not fit the register file).  gate(kc) runs after the MFMAs of step kc, so that the
+  // SiLU-gate VALU work it is given issues between this wave's MFMAs.
+  auto first_half = [&](const unsigned char *base, int u, f32x4(&z1)[2], f32x4(&z3)[2], auto &&gate)
+                        __attribute__((always_inline)) {
+    constexpr int RA = 2;
     bf16x8 ra1[RA], ra3[RA];
-    auto rd = [&](int q, int slot) __attribute__((always_inline)) {
-      // one XOR per read rather than held addresses
-      const unsigned char *pa = base + xor_here(base_a[q / KC], 64 * (q % KC));
+    auto rd = [&](int kc, int slot) __attribute__((always_inline)) {
+      const unsigned char *pa = base + xor_here(base_a[u], 64 * kc);
       ra1[slot] = *reinterpret_cast<const bf16x8 *>(pa);
       ra3[slot] = *reinterpret_cast<const bf16x8 *>(pa + L::kTile);
     };
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int t = 0; t < 2; ++t) z1[t] = z3[t] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) z1[u][t] = z3[u][t] = f32x4{0, 0, 0, 0};
+    for (int q = 0; q < RA - 1 && q < KC; ++q) rd(q, q);
 #pragma unroll
-    for (int q = 0; q < RA - 1; ++q) rd(q, q);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (q + RA - 1 < NQ) rd(q + RA - 1, (q + RA - 1) % RA);
-      const int u = q / KC, kc = q % KC, sl = q % RA;
+    for (int kc = 0; kc < KC; ++kc) {
+      if (kc + RA - 1 < KC) rd(kc + RA - 1, (kc + RA - 1) % RA);
+      const int sl = kc % RA;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        z1[u][t] = mma(ra1[sl], qf[t][kc], z1[u][t]);
-        z3[u][t] = mma(ra3[sl], qf[t][kc], z3[u][t]);
+        z1[t] = mma(ra1[sl], qf[t][kc], z1[t]);
+        z3[t] = mma(ra3[sl], qf[t][kc], z3[t]);
       }
+      gate(kc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // H = SiLU(z1) o z3; element v = 4u + r is hidden 8g + v of the chunk
-    bf16x8 hf[2];
+  };
+  // H of one hidden half: h[t][r] = SiLU(z1) z3 of hidden 8g + 4u + r, token 16t + li.
+  // The 8 elements per lane are spread over the KC steps of the product that hides them.
+  auto gate_part = [&](int kc, const f32x4(&z1)[2], const f32x4(&z3)[2], bf16x4(&h)[2])
+                       __attribute__((always_inline)) {
+    constexpr int EPS = 8 / KC;   // elements per step
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float hv[8];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float z = z1[u][t][r];
-          hv[4 * u + r] = z * sigmoid_fast(z) * z3[u][t][r];
-        }
-      hf[t] = pack8<__bf16>(hv);
+    for (int e = EPS * kc; e < EPS * (kc + 1); ++e) {
+      const int t = e >> 2, r = e & 3;
+      const float z = z1[t][r];
+      h[t][r] = (__bf16)(z * sigmoid_fast(z) * z3[t][r]);
     }
-    // O^T[d][tok] += W2[d][chunk] H^T
-    // the transposing reads run kRing column blocks ahead of their MFMAs (a read's
-    // latency is longer than the two MFMAs it feeds)
-    constexpr int kRing = 8;
+  };
+  // O^T[d][tok] += W2[d][chunk] H^T for the chunk staged at `base`; the transposing
+  // reads run kRing column blocks ahead of their MFMAs.
+  auto second = [&](const unsigned char *base, const bf16x4(&h0)[2], const bf16x4(&h1)[2])
+                    __attribute__((always_inline)) {
+    const bf16x8 hf0 = cat8(h0[0], h1[0]), hf1 = cat8(h0[1], h1[1]);
+    constexpr int kRing = 6;
     bf16x4 wlo[kRing], whi[kRing];
     auto rd_w2 = [&](int dt) __attribute__((always_inline)) {
       wlo[dt % kRing] = lds_read_tr16(base + xor_here(base_b[0], 32 * dt));
@@ -167,40 +172,77 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
     for (int dt = 0; dt < DT; ++dt) {
       if (dt + kRing - 1 < DT) rd_w2(dt + kRing - 1);
       const bf16x8 w2f = cat8(wlo[dt % kRing], whi[dt % kRing]);
-      acc[dt][0] = mma(w2f, hf[0], acc[dt][0]);
-      acc[dt][1] = mma(w2f, hf[1], acc[dt][1]);
+      acc[dt][0] = mma(w2f, hf0, acc[dt][0]);
+      acc[dt][1] = mma(w2f, hf1, acc[dt][1]);
     }
   };
 
+  // Software pipeline over the 32-unit chunks, three stages: iteration c runs
+  //   A: first product of half 0 of chunk c, hiding the gate of half 1 of chunk c - 1;
+  //   B: the second product of chunk c - 1 (its W2^T still in the previous stage);
+  //   C: first product of half 1 of chunk c, hiding the gate of half 0 of chunk c;
+  // and the DMA of chunk c + 1 into the stage chunk c - 2 left.
   const int nch = p.m / kHidChunk;
+  f32x4 za1[2], za3[2];   // half 0 of chunk c (made in A, gated in C)
+  f32x4 zb1[2], zb3[2];   // half 1 of chunk c (made in C, gated in A of the next chunk)
+  bf16x4 h0[2], h1[2];    // H of the chunk waiting for its second product
+  auto no_gate = [](int) __attribute__((always_inline)) {};
+  auto iter = [&](int c, const unsigned char *cur, const unsigned char *prev, unsigned char *next)
+                  __attribute__((always_inline)) {
+    if (c + 1 < nch) stage_chunk(c + 1, next);
+    first_half(cur, 0, za1, za3, [&](int kc) __attribute__((always_inline)) { gate_part(kc, zb1, zb3, h1); });
+    second(prev, h0, h1);
+    first_half(cur, 1, zb1, zb3, [&](int kc) __attribute__((always_inline)) { gate_part(kc, za1, za3, h0); });
+    wait_all_memory();
+    __syncthreads();
+  };
   stage_chunk(0, sa);
   wait_all_memory();
   __syncthreads();
-  for (int hc = 0; hc < nch; hc += 2) {
-    if (hc + 1 < nch) stage_chunk(hc + 1, sb);
-    compute(sa);
-    wait_all_memory();
-    __syncthreads();
-    if (hc + 1 < nch) {
-      if (hc + 2 < nch) stage_chunk(hc + 2, sa);
-      compute(sb);
-      wait_all_memory();
-      __syncthreads();
-    }
+  if (nch > 1) stage_chunk(1, sb);
+  first_half(sa, 0, za1, za3, no_gate);
+  first_half(sa, 1, zb1, zb3, [&](int kc) __attribute__((always_inline)) { gate_part(kc, za1, za3, h0); });
+  wait_all_memory();
+  __syncthreads();
+  for (int c = 1; c < nch; c += 3) {
+    iter(c, sb, sa, sc);
+    if (c + 1 < nch) iter(c + 1, sc, sb, sa);
+    if (c + 2 < nch) iter(c + 2, sa, sc, sb);
   }
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) gate_part(kc, zb1, zb3, h1);
+  const int last = (nch - 1) % 3;
+  second(last == 0 ? sa : last == 1 ? sb : sc, h0, h1);
 
-  // O[tok][16 dt + 4g + r] for r = 0..3: one 8-byte store per (dt, t)
+  // O goes out through LDS: each wave writes its 32 x D bf16 tile (row = token) into a
+  // region of its own, then stores whole rows with 16-byte lanes (every store
+  // instruction covers 1 KB of consecutive rows).  16-byte chunk c of row r sits at
+  // position c ^ (r % 16) of the row (r % NC for rows of fewer than 16 chunks), so
+  // the 8-byte writes of 16 rows at one chunk hit distinct banks.
+  __syncthreads();   // every wave is done with the stages
+  {
+    constexpr int RB = 2 * D, NC = D / 8, SW = (NC < 16 ? NC : 16) - 1, RPI = 1024 / RB;
+    unsigned char *ot = (w < 3 ? sa : w < 6 ? sb : sc) + (w % 3) * 32 * RB;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int64_t tok = tok0 + 16 * t + li;
-    if (tok >= p.nq) continue;
-    __bf16 *O = static_cast<__bf16 *>(p.o) + tok * p.ldo + (int64_t)h * D + 4 * g;
+    for (int t = 0; t < 2; ++t) {
+      const int r = 16 * t + li;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      bf16x4 v;
+      for (int dt = 0; dt < DT; ++dt) {
+        bf16x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[dt][t][r];
-      *reinterpret_cast<bf16x4 *>(O + 16 * dt) = v;
+        for (int q = 0; q < 4; ++q) v[q] = (__bf16)acc[dt][t][q];
+        const int c = 2 * dt + (g >> 1);
+        *reinterpret_cast<bf16x4 *>(ot + r * RB + 16 * (c ^ (r & SW)) + 8 * (g & 1)) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));   // lgkmcnt(0): this wave's tile is in LDS
+#pragma unroll
+    for (int j = 0; j < 32 / RPI; ++j) {
+      const int r = RPI * j + l / NC, c = l % NC;
+      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(ot + r * RB + 16 * (c ^ (r & SW)));
+      const int64_t tok = tok0 + r;
+      if (tok < p.nq)
+        *reinterpret_cast<bf16x8 *>(static_cast<__bf16 *>(p.o) + tok * p.ldo + (int64_t)h * D + 8 * c) = v;
     }
   }
 }
