@@ -33,10 +33,12 @@ namespace {
 //   waves 0-3 ("forward"): z1, z3, p of a block for 16 hidden units each (MFMA,
 //     weights in registers, K/V fragments from LDS), then the SwiGLU backward (VALU);
 //     the packed bf16 operands dZ1, dZ3, H' go to one of two LDS buffers;
-//   waves 4 .. 3 + 4 CS ("contraction"): the token contractions of the previous block
-//     for the same hidden units, CS waves per hidden group, each with D / CS of the
-//     output columns and their fp32 accumulators G1, G3, G2 in registers; these
-//     waves also issue all of the staging DMA.
+//   waves 4 .. 3 + 4 CS ("contraction"): the token contractions of the previous block,
+//     each wave for two hidden groups (32 units) and D / (2 CS) of the output columns,
+//     with their fp32 accumulators G1, G3, G2 in registers: every transposed K / V
+//     fragment it reads from LDS feeds six products (with one hidden group per wave,
+//     three, and the LDS reads per block were 26% higher); these waves also issue all
+//     of the staging DMA.
 // K and V of a block are DMA'd into LDS once (row-major, swizzled) into one of four
 // stages, with the block's rates; the forward waves read 16-byte d-fragments, the
 // contraction waves read the tile transposed (ds_read_b64_tr_b16).
@@ -58,7 +60,8 @@ constexpr int kPkBytes = 4 * 3 * 64 * 16;
 typedef unsigned long long u64;
 typedef u64 u64x2 __attribute__((ext_vector_type(2)));
 
-// contraction waves per hidden group (each takes D / kGradCS of the output columns)
+// 4 kGradCS contraction waves: each takes two of the four hidden groups and
+// D / (2 kGradCS) of the output columns
 constexpr int kGradCS = 2;
 
 template <int D, int CS>
@@ -66,7 +69,6 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
   using L = FastLayout<D>;
   constexpr int KC = D / 32;   // reduction chunks over d
   constexpr int DT = D / 16;   // 16-wide d tiles of the outputs
-  constexpr int DTW = DT / CS; // d tiles per contraction wave
   constexpr int FR = CS == 1 ? 3 : 2;   // forward read ring (registers are scarcer at 3 waves per SIMD)
   // separate arrays (not one indexed array), each named statically, so that the
   // compiler can tell the stages apart
@@ -92,7 +94,6 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
   const bool forward_role = wv < 4;
   const int w = wv & 3;                 // hidden group (both roles)
   const int c = wv - 4;                 // contraction wave index 0 .. 4 CS - 1
-  const int dh = c >> 2;                // its part of d: tiles dh DTW .. dh DTW + DTW - 1
   const int l = tid & 63, g = l >> 4, li = l & 15;
   const int hid0 = jt * kHidTile + 16 * w;
 
@@ -298,9 +299,15 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     if (i + 1 < iters) step(i + 1, st1, pkb1);
     if (i + 2 < iters) step(i + 2, st2, pkb0);
   } else {
-    f32x4 a1[DTW], a3[DTW], a2[DTW];
+    // contraction wave c: hidden groups 2 pr and 2 pr + 1, d tiles DTQ dq .. DTQ dq + DTQ - 1,
+    // so that every transposed K / V fragment feeds six products
+    constexpr int DTQ = DT / (2 * CS);
+    const int pr = c & 1, dq = c >> 1;
+    f32x4 a1[2][DTQ], a3[2][DTQ], a2[2][DTQ];
 #pragma unroll
-    for (int t = 0; t < DTW; ++t) a1[t] = a3[t] = a2[t] = f32x4{0, 0, 0, 0};
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int t = 0; t < DTQ; ++t) a1[e][t] = a3[e][t] = a2[e][t] = f32x4{0, 0, 0, 0};
     // transposed reads: lane (g, li) supplies row 8g + 4q + li/4, column 16 dt + 4 (li % 4)
     // and receives rows 8g + 4q .. +3 of column 16 dt + li; chunk 2dt + e of row r with
     // swizzle s: ((2dt + e) ^ s) * 16 = (16 (e ^ s)) ^ 32 dt
@@ -309,13 +316,14 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     for (int q = 0; q < 2; ++q) {
       const int row = 8 * g + 4 * q + (li >> 2);
       const int e = (li & 3) >> 1;
-      // tile dt0 + j of this wave: 32 (dt0 + j) = 32 dt0 ^ 32 j (dt0 is a multiple of DTW > j)
-      base_b[q] = (row * L::kRowBytes + 16 * (e ^ (swz_kv(row) & (L::kChunks - 1))) + 8 * (li & 1)) ^ (32 * DTW * dh);
+      // tile dt0 + j of this wave: 32 (dt0 + j) = 32 dt0 ^ 32 j (dt0 is a multiple of DTQ > j)
+      base_b[q] = (row * L::kRowBytes + 16 * (e ^ (swz_kv(row) & (L::kChunks - 1))) + 8 * (li & 1)) ^ (32 * DTQ * dq);
     }
     // G1 += dZ1^T K, G3 += dZ3^T K, G2 += V^T H' for the block in stage `blk` with its
     // packed operands pk1, pk3, pkh; the transposed reads run one 16-column tile ahead
     // (scheduling barrier per tile)
-    auto contract_block = [&](const unsigned char *blk, const bf16x8 pk1, const bf16x8 pk3, const bf16x8 pkh) {
+    auto contract_block = [&](const unsigned char *blk, const bf16x8 (&pk1)[2], const bf16x8 (&pk3)[2],
+                              const bf16x8 (&pkh)[2]) {
       bf16x8 ktf[2], vtf[2];
       auto ldb = [&](int dt, int slot) {
         // each address is formed (one XOR) right before its read instead of 32 of them
@@ -328,12 +336,15 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
       };
       ldb(0, 0);
 #pragma unroll
-      for (int dt = 0; dt < DTW; ++dt) {
-        if (dt + 1 < DTW) ldb(dt + 1, (dt + 1) & 1);
+      for (int dt = 0; dt < DTQ; ++dt) {
+        if (dt + 1 < DTQ) ldb(dt + 1, (dt + 1) & 1);
         const int s = dt & 1;
-        a1[dt] = mma(pk1, ktf[s], a1[dt]);
-        a3[dt] = mma(pk3, ktf[s], a3[dt]);
-        a2[dt] = mma(vtf[s], pkh, a2[dt]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          a1[e][dt] = mma(pk1[e], ktf[s], a1[e][dt]);
+          a3[e][dt] = mma(pk3[e], ktf[s], a3[e][dt]);
+          a2[e][dt] = mma(vtf[s], pkh[e], a2[e][dt]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -344,9 +355,14 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     // would make the compiler wait for the DMA first.
     auto step = [&](int i, const unsigned char *ctr, unsigned char *dma, const unsigned char *pkr) {
       const bool issue = i + 2 < nb;
-      const bf16x8 pk1 = *reinterpret_cast<const bf16x8 *>(pkr + pk_slot);
-      const bf16x8 pk3 = *reinterpret_cast<const bf16x8 *>(pkr + pk_slot + 1024);
-      const bf16x8 pkh = *reinterpret_cast<const bf16x8 *>(pkr + pk_slot + 2048);
+      bf16x8 pk1[2], pk3[2], pkh[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const unsigned char *ps = pkr + (((2 * pr + e) * 3) * 64 + l) * 16;
+        pk1[e] = *reinterpret_cast<const bf16x8 *>(ps);
+        pk3[e] = *reinterpret_cast<const bf16x8 *>(ps + 1024);
+        pkh[e] = *reinterpret_cast<const bf16x8 *>(ps + 2048);
+      }
       if (issue) stage_block(blk0 + i + 2, dma);
       // always true here; written as a test because the unconditional form makes
       // the register allocator spill accumulators at d = 256
@@ -374,16 +390,20 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     float *P1 = p.part + ((int64_t)split * 3 * p.heads + h) * mat;
     float *P3 = P1 + p.heads * mat;
     float *P2 = P3 + p.heads * mat;
-    const int dt0 = DTW * dh;
+    const int dt0 = DTQ * dq;
 #pragma unroll
-    for (int j = 0; j < DTW; ++j)
+    for (int e = 0; e < 2; ++e) {
+      const int hid = jt * kHidTile + 16 * (2 * pr + e);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int dt = dt0 + j;
-        P1[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a1[j][r];
-        P3[(int64_t)(hid0 + 4 * g + r) * D + 16 * dt + li] = a3[j][r];
-        P2[(int64_t)(16 * dt + 4 * g + r) * p.m + hid0 + li] = a2[j][r];
-      }
+      for (int j = 0; j < DTQ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int dt = dt0 + j;
+          P1[(int64_t)(hid + 4 * g + r) * D + 16 * dt + li] = a1[e][j][r];
+          P3[(int64_t)(hid + 4 * g + r) * D + 16 * dt + li] = a3[e][j][r];
+          P2[(int64_t)(16 * dt + 4 * g + r) * p.m + hid + li] = a2[e][j][r];
+        }
+    }
   }
 }
 
