@@ -37,8 +37,8 @@ namespace {
 //     each wave for two hidden groups (32 units) and D / (2 CS) of the output columns,
 //     with their fp32 accumulators G1, G3, G2 in registers: every transposed K / V
 //     fragment it reads from LDS feeds six products (with one hidden group per wave,
-//     three, and the LDS reads per block were 26% higher); these waves also issue all
-//     of the staging DMA.
+//     three, and the LDS reads per block were 26% higher); four of these waves, one
+//     per SIMD, also issue all of the staging DMA.
 // K and V of a block are DMA'd into LDS once (row-major, swizzled) into one of four
 // stages, with the block's rates; the forward waves read 16-byte d-fragments, the
 // contraction waves read the tile transposed (ds_read_b64_tr_b16).
@@ -116,7 +116,9 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
   // reads wait for it.
   constexpr int kRowsPer = 1024 / L::kRowBytes;           // token rows per 1 KB piece
   constexpr int NPIECE = 2 * L::kTile / 1024;             // K and V pieces per stage
-  constexpr int PPW = NPIECE / 2 >= 4 * CS ? NPIECE / 2 / (4 * CS) : 1;   // K pieces per DMA wave
+  // four DMA waves, one per SIMD, so that the other contraction wave of each SIMD
+  // starts its products while the copies issue (all eight copying: 1% slower)
+  constexpr int PPW = NPIECE / 2 >= 4 ? NPIECE / 2 / 4 : 1;   // K pieces per DMA wave
   constexpr int NDMA = NPIECE / 2 / PPW;                  // contraction waves that DMA
   const __bf16 *Kh = static_cast<const __bf16 *>(p.k) + (int64_t)h * D;
   const __bf16 *Vh = static_cast<const __bf16 *>(p.v) + (int64_t)h * D;
