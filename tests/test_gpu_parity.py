@@ -74,6 +74,14 @@ def test_other_fast_widths(d, m):
     _check(cfg_like("c4", heads=2, d=d, m=m), n=777, nq_extra=3)
 
 
+@pytest.mark.parametrize("d,m", [(256, 64), (256, 192), (256, 320), (256, 448), (128, 192), (64, 320)])
+def test_fast_kernels_hidden_sizes(d, m):
+    # hidden sizes whose 32-unit chunk count (2, 6, 10, 14) leaves the apply kernel's
+    # three-stage pipeline ending in each of its stages, and odd hidden-tile counts
+    # for the gradient kernel's block map
+    _check(cfg_like("c4", heads=2, d=d, m=m), n=500, nq_extra=41)
+
+
 def test_tttlrm_width_768():
     # the tttLRM head (d = m = 768): the wide-head kernels (big_* in bigd.hip)
     from test_weight_layers_amd.configs import CONFIGS
