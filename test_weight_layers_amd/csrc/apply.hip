@@ -115,8 +115,9 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
 
   // First product for hidden half u (tile rows perm_row(u, .)) of the chunk staged at
   // `base`: z1, z3 for the two token tiles, over d in KC steps; the W1 / W3 fragment
-  // reads run one step ahead (a deeper ring does not fit the register file).  gate(kc) runs after the MFMAs of step kc, so that the
-  // SiLU-gate VALU work it is given issues between this wave's MFMAs.
+  // reads run one step ahead (a deeper ring does not fit the register file).
+  // gate(kc) runs after the MFMAs of step kc, so that the SiLU-gate VALU work it is
+  // given issues between this wave's MFMAs.
   auto first_half = [&](const unsigned char *base, int u, f32x4(&z1)[2], f32x4(&z3)[2], auto &&gate)
                         __attribute__((always_inline)) {
     constexpr int RA = 2;
