@@ -27,7 +27,8 @@ struct Vec8<__bf16> {
     for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
   }
   static __device__ __forceinline__ void store(__bf16 *p, const float *v) {
-    *reinterpret_cast<bf16x8 *>(p) = pack8<__bf16>(v);
+    // V' is not read again by this kernel: a streaming (non-temporal) store
+    __builtin_nontemporal_store(pack8<__bf16>(v), reinterpret_cast<bf16x8 *>(p));
   }
 };
 template <>
@@ -38,8 +39,8 @@ struct Vec8<float> {
     for (int i = 0; i < 8; ++i) v[i] = x[i];
   }
   static __device__ __forceinline__ void store(float *p, const float *v) {
-    *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(p + 4));
   }
 };
 
