@@ -258,7 +258,8 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
       bf16x8 y;
 #pragma unroll
       for (int u = 0; u < 8; ++u) y[u] = (__bf16)((u < 4 ? g0[u] : g1[u - 4]) * (float)xs[i][u] * ri * (float)sz[u]);
-      if (tok < p.n) *reinterpret_cast<bf16x8 *>(out + tok * p.ld_out + ch) = y;
+      // the gated rows are not read again here: streaming (non-temporal) stores
+      if (tok < p.n) __builtin_nontemporal_store(y, reinterpret_cast<bf16x8 *>(out + tok * p.ld_out + ch));
     }
   } else {
     __syncthreads();
