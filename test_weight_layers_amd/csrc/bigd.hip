@@ -238,7 +238,9 @@ __global__ __launch_bounds__(FwdGeo::kThreads) void big_fwd_kernel(BigFwdParams 
     const int tr = rem >> 4, cu = rem & 15;
     const __bf16 *srcs = k == 0 ? o1 : (k == 1 ? o3 : oh);
     const bf16x8 v = *reinterpret_cast<const bf16x8 *>(srcs + st128(tr, 8 * cu));
-    *reinterpret_cast<bf16x8 *>(dst + k * plane + (int64_t)tr * m + 8 * cu) = v;
+    // the intermediates are read by the next kernel, far beyond what the caches hold:
+    // streaming (non-temporal) stores
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x8 *>(dst + k * plane + (int64_t)tr * m + 8 * cu));
   }
 }
 
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(512) void big_hidden_kernel(BigApplyParams p) {
     const int tr = v >> 4, cu = v & 15;
     const __bf16 *hs = it < 4 ? hs0 : hs1;
     const bf16x8 x = *reinterpret_cast<const bf16x8 *>(hs + st128(tr & 127, 8 * cu));
-    *reinterpret_cast<bf16x8 *>(dst + (int64_t)tr * m + 8 * cu) = x;
+    __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(dst + (int64_t)tr * m + 8 * cu));
   }
 }
 
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(512) void big_out_kernel(BigApplyParams p) {
     const int tr = v >> 5, cu = v & 31;           // 256 rows x 32 vectors
     const int64_t tok = tok0 + tr;
     const bf16x8 x = *reinterpret_cast<const bf16x8 *>(orow(it >> 2) + st256(tr & 63, 8 * cu));
-    if (tok < p.nq) *reinterpret_cast<bf16x8 *>(out + tok * p.ldo + 8 * cu) = x;
+    if (tok < p.nq) __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(out + tok * p.ldo + 8 * cu));
   }
 }
 
