@@ -159,37 +159,70 @@ __global__ __launch_bounds__(256) void ns_step_kernel(const float *__restrict__ 
   }
 }
 
-// Weight copies.  W2 [H][d][m] -> W2^T [H][m][d] goes through a 32x32 LDS tile.
+// Weight copies in one launch: W1, W3 (and W2 when asked) cast row for row, 2048
+// elements per workgroup, then W2 [H][d][m] -> W2^T [H][m][d] through 32x32 LDS tiles.
+// A null output skips its part (its workgroups return at once).
 template <typename T>
-__global__ __launch_bounds__(256) void cast_rows_kernel(const float *__restrict__ w, T *__restrict__ o, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) o[i] = from_f32<T>(w[i]);
-}
+struct CastJob {
+  const float *src[3];
+  T *dst[3];            // W1, W3, W2 copies in their own layout
+  T *w2t;               // W2^T copy
+  int64_t n;            // elements per matrix (H d m, a multiple of 2048)
+  int row_blocks;       // n / 2048
+  int heads, d, m;
+};
+constexpr int kCastChunk = 2048;
 
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_cast_kernel(const float *__restrict__ w2, T *__restrict__ w2t,
-                                                             int d, int m) {
+__global__ __launch_bounds__(256) void cast_kernel(CastJob<T> p) {
   __shared__ float tile[32][33];
-  const int h = blockIdx.z;
-  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;     // rows of W2 (d), cols (m)
-  const float *src = w2 + (int64_t)h * d * m;
-  T *dst = w2t + (int64_t)h * d * m;
+  int blk = blockIdx.x;
+  if (blk < 3 * p.row_blocks) {
+    const int j = blk / p.row_blocks;
+    T *o = p.dst[j];
+    if (o == nullptr) return;
+    const int64_t e = (int64_t)(blk % p.row_blocks) * kCastChunk + threadIdx.x * 8;
+    const float *w = p.src[j] + e;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(w), b = *reinterpret_cast<const f32x4 *>(w + 4);
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 v;
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        v[z] = (__bf16)a[z];
+        v[4 + z] = (__bf16)b[z];
+      }
+      *reinterpret_cast<bf16x8 *>(o + e) = v;
+    } else {
+      *reinterpret_cast<f32x4 *>(o + e) = a;
+      *reinterpret_cast<f32x4 *>(o + e + 4) = b;
+    }
+    return;
+  }
+  if (p.w2t == nullptr) return;
+  blk -= 3 * p.row_blocks;
+  const int tc = p.m / 32, tr = p.d / 32;
+  const int h = blk / (tr * tc), rem = blk % (tr * tc);
+  const int r0 = (rem / tc) * 32, c0 = (rem % tc) * 32;    // rows of W2 (d), cols (m)
+  const float *src = p.src[2] + (int64_t)h * p.d * p.m;
+  T *dst = p.w2t + (int64_t)h * p.d * p.m;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int r = ty; r < 32; r += 8) tile[r][tx] = src[(int64_t)(r0 + r) * m + c0 + tx];
+  for (int r = ty; r < 32; r += 8) tile[r][tx] = src[(int64_t)(r0 + r) * p.m + c0 + tx];
   __syncthreads();
-  for (int r = ty; r < 32; r += 8) dst[(int64_t)(c0 + r) * d + r0 + tx] = from_f32<T>(tile[tx][r]);
+  for (int r = ty; r < 32; r += 8) dst[(int64_t)(c0 + r) * p.d + r0 + tx] = from_f32<T>(tile[tx][r]);
 }
 
 template <typename T>
 hipError_t cast_impl(const float *w1, const float *w3, const float *w2, void *w1o, void *w3o, void *w2to,
                      void *w2o, int heads, int d, int m, hipStream_t s) {
-  const int64_t n = (int64_t)heads * d * m;
-  const int grid = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-  if (w1o) hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid), dim3(256), 0, s, w1, static_cast<T *>(w1o), n);
-  if (w3o) hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid), dim3(256), 0, s, w3, static_cast<T *>(w3o), n);
-  if (w2o) hipLaunchKernelGGL(cast_rows_kernel<T>, dim3(grid), dim3(256), 0, s, w2, static_cast<T *>(w2o), n);
-  if (w2to)
-    hipLaunchKernelGGL(transpose_cast_kernel<T>, dim3(m / 32, d / 32, heads), dim3(256), 0, s, w2,
-                       static_cast<T *>(w2to), d, m);
+  CastJob<T> p{};
+  p.src[0] = w1, p.src[1] = w3, p.src[2] = w2;
+  p.dst[0] = static_cast<T *>(w1o), p.dst[1] = static_cast<T *>(w3o), p.dst[2] = static_cast<T *>(w2o);
+  p.w2t = static_cast<T *>(w2to);
+  p.n = (int64_t)heads * d * m;
+  p.row_blocks = (int)(p.n / kCastChunk);
+  p.heads = heads, p.d = d, p.m = m;
+  const int64_t blocks = 3LL * p.row_blocks + (w2to ? (int64_t)heads * (d / 32) * (m / 32) : 0);
+  hipLaunchKernelGGL(cast_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
