@@ -76,6 +76,26 @@ def grad_source_digest():
     return h.hexdigest()
 
 
+def measured_mfma_peak(iters: int = 16384, reps: int = 5) -> float:
+    """Dense bf16 MFMA rate (TFLOP/s) of the library's register-only probe kernel, timed
+    with events on the current stream after two warm-up launches (median of `reps`)."""
+    import numpy as np
+    import torch
+    from test_weight_layers_amd import ttt
+    for _ in range(2):
+        ttt.mfma_rate_probe(iters)
+    torch.cuda.synchronize()
+    rates = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f = ttt.mfma_rate_probe(iters)
+        e1.record()
+        e1.synchronize()
+        rates.append(f / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return float(np.median(rates))
+
+
 def measured_traffic(d):
     """HBM bytes per launch of the gradient kernel from the committed rocprofv3 counter summary,
     or None when the kernel's source changed since the counters were taken (or d differs)."""
@@ -496,6 +516,14 @@ def main():
             conv_bytes = 2.0 * n * H * d * inp.v.element_size()
             out["conv_kernel"] = {"achieved_gbs": conv_bytes / c_avg / 1e9, "peak_gbs": PEAK_HBM_GBS,
                                   "frac": conv_bytes / c_avg / 1e9 / PEAK_HBM_GBS, "avg_launch_ms": c_avg * 1e3}
+        if dt == torch.bfloat16:
+            # the matrix cores' sustained dense bf16 rate on this machine (register-only MFMA
+            # chains on every SIMD), next to the published peak the fractions above use
+            p_meas = measured_mfma_peak()
+            out["mfma_peak_measured"] = {"tflops": p_meas, "published_tflops": peak,
+                                         "probe": "ttt_mfma_rate_probe, 16384 rounds x 8 chains per wave, "
+                                                  "2 waves per SIMD, median of 5 launches"}
+            out["mfma_pct_gemm_phases_of_measured_peak"] = 100.0 * gemm_flops / (gemm_ms * 1e-3) / (p_meas * 1e12)
     if marks:
         out["per_call_ms"] = per_call_stats(marks)
     if not args.no_cpu_baseline:

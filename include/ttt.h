@@ -316,6 +316,17 @@ int ttt_profile_enable(int32_t on);
 int ttt_profile_reset(void);
 int ttt_profile_read(int32_t kind, double *total_ms, int64_t *launches);
 
+/*
+ * ttt_mfma_rate_probe -- a measurement aid, not a step of the layer: launches, on
+ * `stream`, one kernel in which every wave of two per SIMD on every compute unit
+ * runs `iters` rounds of 8 independent 16x16x32 bf16 MFMA chains on register
+ * operands (no memory traffic).  *flop (HOST) receives the launch's FLOP count
+ * (2 x multiply-adds); the caller times the launch (e.g. with events on `stream`)
+ * to get the matrix cores' sustained dense bf16 rate at the clock the chip keeps
+ * under that load.  iters < 1 or flop == NULL: TTT_EINVAL, nothing launched.
+ */
+int ttt_mfma_rate_probe(int32_t iters, void *stream, double *flop);
+
 #ifdef __cplusplus
 }
 #endif

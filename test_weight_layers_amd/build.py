@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libttt.so")
-SOURCES = ("grad.hip", "apply.hip", "ns.hip", "conv.hip", "gate.hip", "bigd.hip", "api.hip")
+SOURCES = ("grad.hip", "apply.hip", "ns.hip", "conv.hip", "gate.hip", "bigd.hip", "probe.hip", "api.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 FLAGS = [

@@ -905,6 +905,13 @@ int ttt_set_option(int32_t option, int64_t value) {
   return fail(TTT_EINVAL, "unknown option %d", option);
 }
 
+int ttt_mfma_rate_probe(int32_t iters, void *stream, double *flop) {
+  if (iters < 1 || !flop) return fail(TTT_EINVAL, "iters must be >= 1 and flop non-null");
+  const hipError_t e = launch_mfma_probe(iters, static_cast<hipStream_t>(stream), flop);
+  if (e != hipSuccess) return fail(TTT_EHIP, "mfma_probe: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
 int ttt_profile_enable(int32_t on) {
   g_prof = on != 0;
   return TTT_OK;

@@ -51,6 +51,10 @@ hipError_t launch_apply(const ApplyParams &p, int d, bool bf16, bool fast, hipSt
 
 // fp32 master W -> operand copies.  w1o/w3o: [H][m][d]; w2to: [H][m][d] (transposed W2);
 // w2o: [H][d][m].  Any output may be null.  bf16 selects the output type.
+// Dense bf16 MFMA rate probe: one launch of `iters` rounds on every compute unit;
+// *flop receives the launch's multiply-add count x 2.
+hipError_t launch_mfma_probe(int iters, hipStream_t s, double *flop);
+
 hipError_t launch_cast(const float *w1, const float *w3, const float *w2, void *w1o, void *w3o,
                        void *w2to, void *w2o, int heads, int d, int m, bool bf16, hipStream_t s);
 

@@ -24,7 +24,7 @@ NORM_PRESERVE = 1
 EXPORTS = ("ttt_last_error", "ttt_update_workspace_bytes", "ttt_apply_workspace_bytes", "ttt_update",
            "ttt_update_ex", "ttt_update_host_workspace_bytes", "ttt_update_host", "ttt_apply", "ttt_output_gate", "ttt_shortconv2d", "ttt_stream_workspace_bytes",
            "ttt_stream", "ttt_stream_ex", "ttt_set_option", "ttt_profile_enable", "ttt_profile_reset",
-           "ttt_profile_read", "ttt_update_noalloc", "ttt_noalloc_scratch_bytes")
+           "ttt_profile_read", "ttt_update_noalloc", "ttt_noalloc_scratch_bytes", "ttt_mfma_rate_probe")
 
 _lib = None
 
@@ -69,6 +69,7 @@ def load() -> ctypes.CDLL:
         "ttt_profile_enable": (ctypes.c_int, [i32]),
         "ttt_profile_reset": (ctypes.c_int, []),
         "ttt_profile_read": (ctypes.c_int, [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+        "ttt_mfma_rate_probe": (ctypes.c_int, [i32, vp, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -395,3 +396,12 @@ def profile_read() -> dict:
         _check(load().ttt_profile_read(i, ctypes.byref(ms), ctypes.byref(cnt)))
         res[name] = (ms.value, cnt.value)
     return res
+
+
+def mfma_rate_probe(iters: int = 16384) -> float:
+    """Launch the dense bf16 MFMA rate probe on the current stream; returns its FLOP count.
+
+    Time the launch with events on the current stream to get the sustained rate."""
+    flop = ctypes.c_double()
+    _check(load().ttt_mfma_rate_probe(int(iters), _stream(), ctypes.byref(flop)))
+    return flop.value

@@ -174,3 +174,10 @@ def test_update_host_argument_errors(lib):
     st = lib.ttt_update_host(1, 64, 128, fake, fake * 2, fake * 3, fake * 4, fake * 5, fake * 6, fake, fake, 64,
                              fake, 0, 10, 5, 0.01, 1, ttt.TTT_F32, 0, None, None, fake, 16, None)
     assert st == -3
+
+
+def test_mfma_rate_probe_argument_errors(lib):
+    flop = ctypes.c_double()
+    assert lib.ttt_mfma_rate_probe(0, None, ctypes.byref(flop)) == -1
+    assert b"iters" in lib.ttt_last_error()
+    assert lib.ttt_mfma_rate_probe(16, None, None) == -1
