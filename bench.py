@@ -76,9 +76,12 @@ def grad_source_digest():
     return h.hexdigest()
 
 
-def measured_mfma_peak(iters: int = 16384, reps: int = 5) -> float:
+def measured_mfma_peak(iters: int = 65536, reps: int = 5) -> float:
     """Dense bf16 MFMA rate (TFLOP/s) of the library's register-only probe kernel, timed
-    with events on the current stream after two warm-up launches (median of `reps`)."""
+    with events on the current stream after two warm-up launches (median of `reps`).
+    65,536 rounds make a launch of about 7 ms: shorter launches read low while the clock
+    ramps up (about 2.07 PFLOP/s at 0.5 ms, 2.29 at 2 ms, 2.41 from 7 ms on, the same
+    over a second of back-to-back launches)."""
     import numpy as np
     import torch
     from test_weight_layers_amd import ttt
@@ -521,7 +524,7 @@ def main():
             # chains on every SIMD), next to the published peak the fractions above use
             p_meas = measured_mfma_peak()
             out["mfma_peak_measured"] = {"tflops": p_meas, "published_tflops": peak,
-                                         "probe": "ttt_mfma_rate_probe, 16384 rounds x 8 chains per wave, "
+                                         "probe": "ttt_mfma_rate_probe, 65536 rounds x 8 chains per wave, "
                                                   "2 waves per SIMD, median of 5 launches"}
             out["mfma_pct_gemm_phases_of_measured_peak"] = 100.0 * gemm_flops / (gemm_ms * 1e-3) / (p_meas * 1e12)
     if marks:
