@@ -309,7 +309,8 @@ int gradient_pass(const UpdatePlan &P, const GradOps &ops, const void *k, const 
 // form).  write_ops: the folded path leaves the operand copies of W_out at the
 // start of the workspace.  grad_out / ns_out: optional copies of G and NS(G).
 int optimiser_step(const UpdatePlan &P, W3 src, W3o out, const float *part, int splits, float lr, bool write_ops,
-                   float *grad_out, float *ns_out, bool norm, char *ws, hipStream_t s) {
+                   float *grad_out, float *ns_out, bool norm, char *ws, hipStream_t s,
+                   hipEvent_t before_write = nullptr) {
   const size_t mat = (size_t)P.H * P.d * P.m;
   void *const wop = ws + P.off_wop;
   float *g = reinterpret_cast<float *>(ws + P.off_g);
@@ -343,7 +344,7 @@ int optimiser_step(const UpdatePlan &P, W3 src, W3o out, const float *part, int 
     np.lr = lr, np.eps = kNsEps, np.a_coef = kNsA, np.b_coef = kNsB, np.c_coef = kNsC;
     np.iters = kNsIters, np.heads = P.H, np.d = P.d, np.m = P.m, np.r = P.r, np.c = P.c;
     np.norm_preserve = norm, np.wsq = wsq;
-    st = run(TTT_K_NS, "newton_schulz", s, [&] { return launch_ns_optimiser(np, P.bf16, s); });
+    st = run(TTT_K_NS, "newton_schulz", s, [&] { return launch_ns_optimiser(np, P.bf16, s, before_write); });
     if (st) return st;
     if (norm) {
       st = run(TTT_K_NS, "norm_rescale", s, [&] {
@@ -353,6 +354,10 @@ int optimiser_step(const UpdatePlan &P, W3 src, W3o out, const float *part, int 
       if (st) return st;
     }
     return TTT_OK;
+  }
+  if (before_write) {   // this path rewrites W_out early: wait before anything
+    const hipError_t e = hipStreamWaitEvent(s, before_write, 0);
+    if (e != hipSuccess) return fail(TTT_EHIP, "hipStreamWaitEvent: %s", hipGetErrorString(e));
   }
   st = run(TTT_K_REDUCE, "reduce", s, [&] {
     return launch_reduce(part, splits, (int64_t)3 * mat, g, grad_out, sumsq, s);
@@ -634,6 +639,25 @@ static int copy_stream(hipStream_t *out) {
   return TTT_OK;
 }
 
+// One side stream per device (default priority, created on first use, kept for the
+// life of the process): a stream's apply of chunk c runs on it while the caller's
+// stream runs chunk c's optimiser step (both read only the weights of chunk c).
+static int side_stream(hipStream_t *out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TTT_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TTT_EUNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(TTT_EHIP, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+  }
+  *out = streams[dev];
+  return TTT_OK;
+}
+
 // Workspace of ttt_update_host: the update plan of one batch, the running G, and
 // two staging slots (K rows, V rows, the batch's rates).
 struct HostPlan {
@@ -839,6 +863,61 @@ int ttt_output_gate(int32_t channels, const void *o_in, int64_t ld_in, const voi
   return run(TTT_K_GATE, "output_gate", s, [&] { return launch_gate(gp, dtype == TTT_BF16, s); });
 }
 
+}  // extern "C"
+
+namespace {
+// The stream with one inner step and the fast apply kernel (bf16, d <= 256): chunk c's
+// gradient runs on the caller's stream, then its apply on the side stream alongside its
+// optimiser step.  Both read only W_c: the apply the shared operand copies, which the
+// step's last product overwrites with W_{c+1}'s, so that product waits for the apply.
+// The next chunk's apply waits for its gradient to be issued after that product.  The
+// results are those of apply-then-update per chunk, bit for bit (same kernels, same
+// inputs); the side stream joins the caller's through the last chunk's step.
+int stream_overlapped(int heads, int d, int m, W3o w, const char *k, const char *v, int64_t ld_kv, const float *eta,
+                      int64_t eta_hs, const char *q, int64_t ld_q, char *o, int64_t ld_o, int64_t n, int64_t chunk,
+                      float lr, bool norm, char *ws, hipStream_t s) {
+  hipStream_t s2 = nullptr;
+  int st = side_stream(&s2);
+  if (st) return st;
+  hipEvent_t ready = nullptr, applied = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&applied, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    if (ready) hipEventDestroy(ready);
+    return fail(TTT_EHIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+  }
+  const size_t es = 2;
+  for (int64_t t0 = 0; t0 < n && !st; t0 += chunk) {
+    const int64_t len = n - t0 < chunk ? n - t0 : chunk;
+    const UpdatePlan P = plan_update(heads, d, m, len, TTT_BF16);
+    float *part = reinterpret_cast<float *>(ws + P.off_part);
+    GradOps ops{};
+    // W_c's operand copies: cast for the first chunk, left by the previous step after it
+    if ((st = prepare_operands(P, W3{w.w1, w.w3, w.w2}, t0 != 0, ws, s, &ops))) break;
+    if ((st = gradient_pass(P, ops, k + t0 * ld_kv * es, v + t0 * ld_kv * es, ld_kv, eta + t0, eta_hs, part, ws, s)))
+      break;
+    if ((e = hipEventRecord(ready, s)) != hipSuccess || (e = hipStreamWaitEvent(s2, ready, 0)) != hipSuccess) {
+      st = fail(TTT_EHIP, "stream event: %s", hipGetErrorString(e));
+      break;
+    }
+    if ((st = do_apply(heads, d, m, W3{w.w1, w.w3, w.w2}, q + t0 * ld_q * es, ld_q, o + t0 * ld_o * es, ld_o, len,
+                       TTT_BF16, ws, s2, true)))
+      break;
+    if ((e = hipEventRecord(applied, s2)) != hipSuccess) {
+      st = fail(TTT_EHIP, "stream event: %s", hipGetErrorString(e));
+      break;
+    }
+    st = optimiser_step(P, W3{w.w1, w.w3, w.w2}, w, part, P.splits, lr, true, nullptr, nullptr, norm, ws, s, applied);
+  }
+  if (st) hipStreamWaitEvent(s, applied, 0);   // an error: still join what was issued
+  hipEventDestroy(ready);
+  hipEventDestroy(applied);
+  return st;
+}
+}  // namespace
+
+extern "C" {
+
 int ttt_stream_ex(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, float *w2, const void *k,
                   const void *v, int64_t ld_kv, const float *eta, int64_t eta_head_stride, const void *q, int64_t ld_q,
                   void *o, int64_t ld_o, int64_t n, int64_t chunk, float lr, int32_t steps, int32_t dtype,
@@ -867,6 +946,10 @@ int ttt_stream_ex(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, flo
   // (when its layout is the same) and gradient read them: one cast per stream.
   const bool carry = !g_ns_unfused;
   const bool shared = carry && apply_shares_update_ops(d, dtype);
+  if (shared && steps == 1 && dtype == TTT_BF16 && !g_force_general && apply_fast_supported(d, true))
+    return stream_overlapped(heads, d, m, W3o{w1, w3, w2}, static_cast<const char *>(k), static_cast<const char *>(v),
+                             ld_kv, eta, eta_head_stride, static_cast<const char *>(q), ld_q, static_cast<char *>(o),
+                             ld_o, n, chunk, lr, (flags & TTT_NORM_PRESERVE) != 0, ws, s);
   for (int64_t t0 = 0; t0 < n; t0 += chunk) {
     const int64_t len = n - t0 < chunk ? n - t0 : chunk;
     const bool first = t0 == 0;

@@ -107,7 +107,10 @@ struct NsStepParams {
   int norm_preserve;
   float *wsq;
 };
-hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s);
+// before_last (optional): an event the stream waits for before the last product, the
+// one that writes W_out and the operand copies (so that work on another stream may
+// read the old copies until then).
+hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s, hipEvent_t before_last = nullptr);
 
 // acc = (first ? 0 : acc) + sum_s part[s * per_split ..] (per_split % 4 == 0), fixed order.
 hipError_t launch_accumulate(float *acc, const float *part, int splits, int64_t per_split, bool first,

@@ -661,7 +661,7 @@ hipError_t rescale_impl(float *w1o, float *w3o, float *w2o, const float *wsq, in
 }
 
 template <typename T>
-hipError_t ns_optimiser_impl(const NsStepParams &p, hipStream_t s) {
+hipError_t ns_optimiser_impl(const NsStepParams &p, hipStream_t s, hipEvent_t before_last) {
   const int B = 3 * p.heads, rt = p.r / kT, ct = p.c / kT;
   hipLaunchKernelGGL(ns_prep_kernel, dim3(B * rt * ct), dim3(256), 0, s, p);
   int cur = 0;
@@ -670,18 +670,23 @@ hipError_t ns_optimiser_impl(const NsStepParams &p, hipStream_t s) {
     const int tri = B * rt * (rt + 1) / 2;      // upper-triangle tiles of the symmetric products
     hipLaunchKernelGGL((ns_tile_kernel<T, 0>), dim3(tri), dim3(256), 0, s, p, cur, first);
     hipLaunchKernelGGL((ns_tile_kernel<T, 1>), dim3(tri), dim3(256), 0, s, p, cur, first);
-    if (it + 1 < p.iters)
+    if (it + 1 < p.iters) {
       hipLaunchKernelGGL((ns_tile_kernel<T, 2>), dim3(B * rt * ct), dim3(256), 0, s, p, cur, first);
-    else
+    } else {
+      if (before_last) {
+        const hipError_t e = hipStreamWaitEvent(s, before_last, 0);
+        if (e != hipSuccess) return e;
+      }
       hipLaunchKernelGGL((ns_tile_kernel<T, 3>), dim3(B * rt * ct), dim3(256), 0, s, p, cur, first);
+    }
     cur ^= 1;
   }
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s) {
-  return bf16 ? ns_optimiser_impl<__bf16>(p, s) : ns_optimiser_impl<float>(p, s);
+hipError_t launch_ns_optimiser(const NsStepParams &p, bool bf16, hipStream_t s, hipEvent_t before_last) {
+  return bf16 ? ns_optimiser_impl<__bf16>(p, s, before_last) : ns_optimiser_impl<float>(p, s, before_last);
 }
 
 hipError_t launch_accumulate(float *acc, const float *part, int splits, int64_t per_split, bool first,
