@@ -268,8 +268,8 @@ int ttt_stream_workspace_bytes(int32_t heads, int32_t d, int32_t m, int64_t chun
  * w1, w3, w2 are updated in place and hold the final state on return.
  * q, o: [n][ld_q] / [n][ld_o]; k, v: [n][ld_kv]; eta as in ttt_update with
  * token index i counted over the whole stream.
- * With steps = 1 and bf16 tokens of d in {64, 128, 256}, each chunk's apply runs on
- * a library-owned side stream beside that chunk's optimiser step (both read only
+ * With bf16 tokens of d in {64, 128, 256}, each chunk's apply runs on a
+ * library-owned side stream beside that chunk's first optimiser step (both read only
  * the chunk's starting weights); every piece of that work is ordered before any
  * work the caller enqueues on `stream` afterwards, and the results are those of
  * the sequential order, bit for bit.

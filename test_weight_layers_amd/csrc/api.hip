@@ -866,16 +866,16 @@ int ttt_output_gate(int32_t channels, const void *o_in, int64_t ld_in, const voi
 }  // extern "C"
 
 namespace {
-// The stream with one inner step and the fast apply kernel (bf16, d <= 256): chunk c's
-// gradient runs on the caller's stream, then its apply on the side stream alongside its
-// optimiser step.  Both read only W_c: the apply the shared operand copies, which the
-// step's last product overwrites with W_{c+1}'s, so that product waits for the apply.
-// The next chunk's apply waits for its gradient to be issued after that product.  The
+// The stream with the fast apply kernel (bf16, d <= 256): chunk c's first gradient runs
+// on the caller's stream, then its apply on the side stream alongside the first
+// optimiser step.  Both read only W_c: the apply the shared operand copies, which that
+// step's last product overwrites, so that product waits for the apply.  The next
+// chunk's apply waits for its gradient to be issued after all of chunk c's steps.  The
 // results are those of apply-then-update per chunk, bit for bit (same kernels, same
-// inputs); the side stream joins the caller's through the last chunk's step.
+// inputs); the side stream joins the caller's through the last chunk's first step.
 int stream_overlapped(int heads, int d, int m, W3o w, const char *k, const char *v, int64_t ld_kv, const float *eta,
                       int64_t eta_hs, const char *q, int64_t ld_q, char *o, int64_t ld_o, int64_t n, int64_t chunk,
-                      float lr, bool norm, char *ws, hipStream_t s) {
+                      float lr, int steps, bool norm, char *ws, hipStream_t s) {
   hipStream_t s2 = nullptr;
   int st = side_stream(&s2);
   if (st) return st;
@@ -891,23 +891,29 @@ int stream_overlapped(int heads, int d, int m, W3o w, const char *k, const char 
     const int64_t len = n - t0 < chunk ? n - t0 : chunk;
     const UpdatePlan P = plan_update(heads, d, m, len, TTT_BF16);
     float *part = reinterpret_cast<float *>(ws + P.off_part);
-    GradOps ops{};
-    // W_c's operand copies: cast for the first chunk, left by the previous step after it
-    if ((st = prepare_operands(P, W3{w.w1, w.w3, w.w2}, t0 != 0, ws, s, &ops))) break;
-    if ((st = gradient_pass(P, ops, k + t0 * ld_kv * es, v + t0 * ld_kv * es, ld_kv, eta + t0, eta_hs, part, ws, s)))
-      break;
-    if ((e = hipEventRecord(ready, s)) != hipSuccess || (e = hipStreamWaitEvent(s2, ready, 0)) != hipSuccess) {
-      st = fail(TTT_EHIP, "stream event: %s", hipGetErrorString(e));
-      break;
+    for (int t = 0; t < steps && !st; ++t) {
+      GradOps ops{};
+      // the operand copies: cast for the stream's first step, left by the previous step after it
+      if ((st = prepare_operands(P, W3{w.w1, w.w3, w.w2}, t0 != 0 || t != 0, ws, s, &ops))) break;
+      if ((st = gradient_pass(P, ops, k + t0 * ld_kv * es, v + t0 * ld_kv * es, ld_kv, eta + t0, eta_hs, part, ws,
+                              s)))
+        break;
+      if (t == 0) {
+        if ((e = hipEventRecord(ready, s)) != hipSuccess || (e = hipStreamWaitEvent(s2, ready, 0)) != hipSuccess) {
+          st = fail(TTT_EHIP, "stream event: %s", hipGetErrorString(e));
+          break;
+        }
+        if ((st = do_apply(heads, d, m, W3{w.w1, w.w3, w.w2}, q + t0 * ld_q * es, ld_q, o + t0 * ld_o * es, ld_o,
+                           len, TTT_BF16, ws, s2, true)))
+          break;
+        if ((e = hipEventRecord(applied, s2)) != hipSuccess) {
+          st = fail(TTT_EHIP, "stream event: %s", hipGetErrorString(e));
+          break;
+        }
+      }
+      st = optimiser_step(P, W3{w.w1, w.w3, w.w2}, w, part, P.splits, lr, true, nullptr, nullptr, norm, ws, s,
+                          t == 0 ? applied : nullptr);
     }
-    if ((st = do_apply(heads, d, m, W3{w.w1, w.w3, w.w2}, q + t0 * ld_q * es, ld_q, o + t0 * ld_o * es, ld_o, len,
-                       TTT_BF16, ws, s2, true)))
-      break;
-    if ((e = hipEventRecord(applied, s2)) != hipSuccess) {
-      st = fail(TTT_EHIP, "stream event: %s", hipGetErrorString(e));
-      break;
-    }
-    st = optimiser_step(P, W3{w.w1, w.w3, w.w2}, w, part, P.splits, lr, true, nullptr, nullptr, norm, ws, s, applied);
   }
   if (st) hipStreamWaitEvent(s, applied, 0);   // an error: still join what was issued
   hipEventDestroy(ready);
@@ -946,10 +952,10 @@ int ttt_stream_ex(int32_t heads, int32_t d, int32_t m, float *w1, float *w3, flo
   // (when its layout is the same) and gradient read them: one cast per stream.
   const bool carry = !g_ns_unfused;
   const bool shared = carry && apply_shares_update_ops(d, dtype);
-  if (shared && steps == 1 && dtype == TTT_BF16 && !g_force_general && apply_fast_supported(d, true))
+  if (shared && dtype == TTT_BF16 && !g_force_general && apply_fast_supported(d, true))
     return stream_overlapped(heads, d, m, W3o{w1, w3, w2}, static_cast<const char *>(k), static_cast<const char *>(v),
                              ld_kv, eta, eta_head_stride, static_cast<const char *>(q), ld_q, static_cast<char *>(o),
-                             ld_o, n, chunk, lr, (flags & TTT_NORM_PRESERVE) != 0, ws, s);
+                             ld_o, n, chunk, lr, steps, (flags & TTT_NORM_PRESERVE) != 0, ws, s);
   for (int64_t t0 = 0; t0 < n; t0 += chunk) {
     const int64_t len = n - t0 < chunk ? n - t0 : chunk;
     const bool first = t0 == 0;

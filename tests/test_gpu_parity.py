@@ -254,15 +254,15 @@ def test_stream_against_oracle(kind):
             assert rel(dw, dw_ref) <= tol
 
 
-@pytest.mark.parametrize("norm", [False, True])
-def test_stream_bit_equals_sequential_calls(norm):
-    # with one step and the fast apply, the stream runs each chunk's apply on a second
-    # stream beside its optimiser step; the result must be that of apply-then-update
-    # per chunk bit for bit (repeated, with a ragged last chunk, so that a missing wait
-    # between the two streams would show)
+@pytest.mark.parametrize("norm,n,chunk,steps", [(False, 20000, 4096, 1), (True, 20000, 4096, 1),
+                                               (False, 8193, 4096, 1), (False, 9000, 4096, 2)])
+def test_stream_bit_equals_sequential_calls(norm, n, chunk, steps):
+    # with the fast apply, the stream runs each chunk's apply on a second stream beside
+    # its first optimiser step; the result must be that of apply-then-update
+    # per chunk bit for bit (repeated, with a ragged last chunk and a one-token one, so
+    # that a missing wait between the two streams would show)
     from test_weight_layers_amd import ttt
     cfg = cfg_like("c4", heads=4, d=256, m=512)
-    n, chunk = 20000, 4096
     inp = synth.make_inputs(cfg, n=n, nq_extra=0)
     d = synth.to_device(inp, "cuda")
     w_seq = tuple(x.clone() for x in (d.w1, d.w3, d.w2))
@@ -270,11 +270,11 @@ def test_stream_bit_equals_sequential_calls(norm):
     for t0 in range(0, n, chunk):
         t1 = min(n, t0 + chunk)
         ttt.apply(w_seq, d.q[t0:t1], out=o_seq[t0:t1])
-        ttt.update(w_seq, d.k[t0:t1], d.v[t0:t1], d.eta[:, t0:t1], cfg.lr, 1, out=w_seq, norm_preserve=norm)
+        ttt.update(w_seq, d.k[t0:t1], d.v[t0:t1], d.eta[:, t0:t1], cfg.lr, steps, out=w_seq, norm_preserve=norm)
     torch.cuda.synchronize()
     for rep in range(3):
         w = tuple(x.clone() for x in (d.w1, d.w3, d.w2))
-        o = ttt.stream(w, d.k, d.v, d.eta, d.q, cfg.lr, 1, chunk, norm_preserve=norm)
+        o = ttt.stream(w, d.k, d.v, d.eta, d.q, cfg.lr, steps, chunk, norm_preserve=norm)
         torch.cuda.synchronize()
         assert torch.equal(o, o_seq), rep
         for a, b in zip(w, w_seq):
