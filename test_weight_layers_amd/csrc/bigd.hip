@@ -81,26 +81,37 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[NP][G::FM][G::FN], cons
   auto issue = [&](int kc, unsigned char *dst) __attribute__((always_inline)) {
     const int kb = kc * 64;
 #pragma unroll
-    for (int q = 0; q < G::kPPW; ++q) copy16_to_lds(src[q] + kb, dst + (w * G::kPPW + q) * 1024);
+    for (int q = 0; q < G::kPPW; ++q) copy16_to_lds_untracked(src[q] + kb, dst + (w * G::kPPW + q) * 1024);
   };
-  auto compute = [&](const unsigned char *stg) __attribute__((always_inline)) {
+  // Products of the stage at `stg`.  The B fragments are read one group (FN x NB
+  // groups, each feeding NP products) ahead; after each group's products
+  // `between(group)` runs (the next chunk's copies are spread over the groups there,
+  // so that the copy path and the matrix cores work at the same time).
+  constexpr int NG = G::NB * G::FN;
+  auto compute = [&](const unsigned char *stg, auto &&between) __attribute__((always_inline)) {
     bf16x8 fa[G::NA][G::FM];
 #pragma unroll
     for (int a = 0; a < G::NA; ++a)
 #pragma unroll
       for (int i = 0; i < G::FM; ++i) fa[a][i] = nt_frag(stg, a * G::TM + wr * G::WM + 16 * i + li, g);
+    auto rd_b = [&](int gi) __attribute__((always_inline)) {
+      const int b = gi / G::FN, j = gi % G::FN;
+      return nt_frag(stg, G::NA * G::TM + b * G::TN + wc * G::WN + 16 * j + li, g);
+    };
+    bf16x8 fb_next = rd_b(0);
 #pragma unroll
-    for (int b = 0; b < G::NB; ++b)
+    for (int gi = 0; gi < NG; ++gi) {
+      const bf16x8 fb = fb_next;
+      if (gi + 1 < NG) fb_next = rd_b(gi + 1);
+      const int b = gi / G::FN, j = gi % G::FN;
 #pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        const bf16x8 fb = nt_frag(stg, G::NA * G::TM + b * G::TN + wc * G::WN + 16 * j + li, g);
+      for (int p = 0; p < NP; ++p)
+        if (pb[p] == b) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-          if (pb[p] == b) {
-#pragma unroll
-            for (int i = 0; i < G::FM; ++i) acc[p][i][j] = mma(fa[pa[p]][i], fb, acc[p][i][j]);
-          }
-      }
+          for (int i = 0; i < G::FM; ++i) acc[p][i][j] = mma(fa[pa[p]][i], fb, acc[p][i][j]);
+        }
+      between(gi);
+    }
   };
   auto step = [&](int kc, const unsigned char *cur, unsigned char *refill) __attribute__((always_inline)) {
     const int later = nk - 1 - kc;        // chunks after kc already issued: min(later, NST - 2)
@@ -111,8 +122,14 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[NP][G::FM][G::FN], cons
     else
       wait_vmcnt<0>();
     bare_barrier();
-    if (kc + G::NST - 1 < nk) issue(kc + G::NST - 1, refill);
-    compute(cur);
+    const bool more = kc + G::NST - 1 < nk;   // wave-uniform
+    const int kb = (kc + G::NST - 1) * 64;
+    // copies q with q * NG / kPPW == gi go after group gi
+    compute(cur, [&](int gi) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < G::kPPW; ++q)
+        if (more && q * NG / G::kPPW == gi) copy16_to_lds_untracked(src[q] + kb, refill + (w * G::kPPW + q) * 1024);
+    });
   };
   unsigned char *const ring[4] = {st0, st1, st2, st3};
 #pragma unroll
@@ -206,14 +223,23 @@ __global__ __launch_bounds__(FwdGeo::kThreads) void big_fwd_kernel(BigFwdParams 
   // SwiGLU backward of element (token row 32 wr + 16 i + 4 g + r, hidden 64 wc + 16 j + li)
   __bf16 *o1 = reinterpret_cast<__bf16 *>(st0), *o3 = reinterpret_cast<__bf16 *>(st1),
          *oh = reinterpret_cast<__bf16 *>(st2);
+  // this lane's rates, all fetched before the first is used (rows past n read row
+  // n - 1 and are zeroed: they contribute nothing)
   const float *eta = p.eta + (int64_t)h * p.eta_hs;
+  float nes[G::FM][4];
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t tok = tok0 + wr * G::WM + 16 * i + 4 * g + r;
+      nes[i][r] = eta[tok < p.n ? tok : p.n - 1];
+    }
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = wr * G::WM + 16 * i + 4 * g + r;
-      const int64_t tok = tok0 + tr;
-      const float ne = tok < p.n ? -eta[tok] : 0.0f;     // rows past n contribute nothing
+      const float ne = tok0 + tr < p.n ? -nes[i][r] : 0.0f;
 #pragma unroll
       for (int j = 0; j < G::FN; ++j) {
         const int uc = wc * G::WN + 16 * j + li;
