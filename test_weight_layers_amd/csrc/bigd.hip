@@ -108,7 +108,7 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[NP][G::FM][G::FN], cons
       for (int p = 0; p < NP; ++p)
         if (pb[p] == b) {
 #pragma unroll
-          for (int i = 0; i < G::FM; ++i) acc[p][i][j] = mma(fa[pa[p]][i], fb, acc[p][i][j]);
+          for (int i = 0; i < G::FM; ++i) acc[p][i][j] = mma(fb, fa[pa[p]][i], acc[p][i][j]);
         }
       between(gi);
     }
@@ -144,11 +144,13 @@ __device__ __forceinline__ void nt_mainloop(f32x4 (&acc)[NP][G::FM][G::FN], cons
   __syncthreads();                        // every wave is done with the ring
 }
 
-// bf16 tile [rows][128] staged for 16-byte stores: element (r, c) of a 256-byte
-// row sits at column c ^ 16 ((r / 4) % 4), so the four row groups of an MFMA
-// accumulator store land on distinct banks.
-__device__ __forceinline__ int st128(int r, int c) { return r * 128 + (c ^ (16 * ((r >> 2) & 3))); }
-__device__ __forceinline__ int st256(int r, int c) { return r * 256 + (c ^ (16 * ((r >> 2) & 3))); }
+// bf16 output tiles [rows][C] (C = 128 or 256) staged in LDS between the products
+// and the 16-byte global stores.  A lane writes four consecutive columns (8 bytes,
+// unit u = column / 4) of one row; unit u of row r sits at u ^ 2 (r % 16), so the 16
+// rows x 2 units that one write instruction serves together fall on distinct banks,
+// and a 16-byte chunk c (units 2c, 2c + 1) stays whole, at c ^ (r % 16).
+template <int C> __device__ __forceinline__ int stage_w(int r, int u) { return r * C + 4 * (u ^ ((r & 15) << 1)); }
+template <int C> __device__ __forceinline__ int stage_r(int r, int c) { return r * C + 8 * (c ^ (r & 15)); }
 
 // ------------------------------------------------------- gradient, forward
 // 8 waves, two per SIMD (a 4-wave layout with 64 x 64 wave tiles and AGPR
@@ -220,38 +222,42 @@ __global__ __launch_bounds__(FwdGeo::kThreads) void big_fwd_kernel(BigFwdParams 
   constexpr int pa[3] = {0, 0, 1}, pb[3] = {0, 1, 2};   // K W1^T, K W3^T, V (W2^T)^T
   nt_mainloop<G, 3>(acc, src, pa, pb, d / 32, st0, st1, st2, st0, w, g, li, wr, wc);
 
-  // SwiGLU backward of element (token row 32 wr + 16 i + 4 g + r, hidden 64 wc + 16 j + li)
+  // SwiGLU backward.  Tile (i, j) holds the products transposed: lane (g, li) has
+  // hidden units 64 wc + 16 j + 4 g + r (r = 0..3) of token row WM wr + 16 i + li.
   __bf16 *o1 = reinterpret_cast<__bf16 *>(st0), *o3 = reinterpret_cast<__bf16 *>(st1),
          *oh = reinterpret_cast<__bf16 *>(st2);
-  // this lane's rates, all fetched before the first is used (rows past n read row
-  // n - 1 and are zeroed: they contribute nothing)
+  // this lane's rates, fetched together (rows past n read row n - 1 and are zeroed:
+  // they contribute nothing)
   const float *eta = p.eta + (int64_t)h * p.eta_hs;
-  float nes[G::FM][4];
+  float nes[G::FM];
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i)
+  for (int i = 0; i < G::FM; ++i) {
+    const int64_t tok = tok0 + wr * G::WM + 16 * i + li;
+    nes[i] = eta[tok < p.n ? tok : p.n - 1];
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t tok = tok0 + wr * G::WM + 16 * i + 4 * g + r;
-      nes[i][r] = eta[tok < p.n ? tok : p.n - 1];
-    }
+  for (int i = 0; i < G::FM; ++i) {
+    const int tr = wr * G::WM + 16 * i + li;
+    const float ne = tok0 + tr < p.n ? -nes[i] : 0.0f;
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i)
+    for (int j = 0; j < G::FN; ++j) {
+      bf16x4 v1, v3, vh;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tr = wr * G::WM + 16 * i + 4 * g + r;
-      const float ne = tok0 + tr < p.n ? -nes[i][r] : 0.0f;
-#pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        const int uc = wc * G::WN + 16 * j + li;
+      for (int r = 0; r < 4; ++r) {
         const float z = acc[0][i][j][r], y = acc[1][i][j][r];
         const float sg = sigmoid_fast(z);
         const float act = z * sg;
         const float dh = ne * acc[2][i][j][r];
-        o1[st128(tr, uc)] = (__bf16)(dh * y * (sg + act - act * sg));
-        o3[st128(tr, uc)] = (__bf16)(dh * act);
-        oh[st128(tr, uc)] = (__bf16)(ne * (act * y));
+        v1[r] = (__bf16)(dh * y * (sg + act - act * sg));
+        v3[r] = (__bf16)(dh * act);
+        vh[r] = (__bf16)(ne * (act * y));
       }
+      const int u = (wc * G::WN + 16 * j) / 4 + g;
+      *reinterpret_cast<bf16x4 *>(o1 + stage_w<G::TN>(tr, u)) = v1;
+      *reinterpret_cast<bf16x4 *>(o3 + stage_w<G::TN>(tr, u)) = v3;
+      *reinterpret_cast<bf16x4 *>(oh + stage_w<G::TN>(tr, u)) = vh;
     }
+  }
   __syncthreads();
   // 3 outputs x 128 rows x 16 vectors of 8 hidden units
   constexpr int VPO = G::TM * 16 / G::kThreads;            // vectors per thread and output
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(FwdGeo::kThreads) void big_fwd_kernel(BigFwdParams 
     const int rem = t + G::kThreads * (it % VPO);
     const int tr = rem >> 4, cu = rem & 15;
     const __bf16 *srcs = k == 0 ? o1 : (k == 1 ? o3 : oh);
-    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(srcs + st128(tr, 8 * cu));
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(srcs + stage_r<G::TN>(tr, cu));
     // the intermediates are read by the next kernel, far beyond what the caches hold:
     // streaming (non-temporal) stores
     __builtin_nontemporal_store(v, reinterpret_cast<bf16x8 *>(dst + k * plane + (int64_t)tr * m + 8 * cu));
@@ -498,21 +504,25 @@ __global__ __launch_bounds__(512) void big_hidden_kernel(BigApplyParams p) {
   constexpr int pa[2] = {0, 0}, pb[2] = {0, 1};
   nt_mainloop<G, 2>(acc, src, pa, pb, d / 32, st0, st1, st2, st3, w, g, li, wr, wc);
 
-  // H = SiLU(z1) o z3, staged as [256 tokens][128 hidden] bf16 in st0 (rows 0..127), st1
+  // H = SiLU(z1) o z3, staged as [256 tokens][128 hidden] bf16 in st0 (rows 0..127), st1;
+  // tile (i, j) holds the products transposed: lane (g, li) has hidden units
+  // 64 wc + 16 j + 4 g + r of token row 64 wr + 16 i + li
   __bf16 *hs0 = reinterpret_cast<__bf16 *>(st0), *hs1 = reinterpret_cast<__bf16 *>(st1);
+  __bf16 *hs = wr < 2 ? hs0 : hs1;
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i)
+  for (int i = 0; i < G::FM; ++i) {
+    const int tr = wr * G::WM + 16 * i + li;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tr = wr * G::WM + 16 * i + 4 * g + r;
-      __bf16 *hs = wr < 2 ? hs0 : hs1;
+    for (int j = 0; j < G::FN; ++j) {
+      bf16x4 v;
 #pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        const int uc = wc * G::WN + 16 * j + li;
+      for (int r = 0; r < 4; ++r) {
         const float z = acc[0][i][j][r];
-        hs[st128(tr & 127, uc)] = (__bf16)(z * sigmoid_fast(z) * acc[1][i][j][r]);
+        v[r] = (__bf16)(z * sigmoid_fast(z) * acc[1][i][j][r]);
       }
+      *reinterpret_cast<bf16x4 *>(hs + stage_w<G::TN>(tr & 127, (wc * G::WN + 16 * j) / 4 + g)) = v;
     }
+  }
   __syncthreads();
   __bf16 *dst = static_cast<__bf16 *>(p.hbuf) + ((int64_t)h * p.nq_pad + tok0) * m + u0;
 #pragma unroll
@@ -520,7 +530,7 @@ __global__ __launch_bounds__(512) void big_hidden_kernel(BigApplyParams p) {
     const int v = t + 512 * it;
     const int tr = v >> 4, cu = v & 15;
     const __bf16 *hs = it < 4 ? hs0 : hs1;
-    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(hs + st128(tr & 127, 8 * cu));
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(hs + stage_r<G::TN>(tr & 127, cu));
     __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(dst + (int64_t)tr * m + 8 * cu));
   }
 }
@@ -566,15 +576,18 @@ __global__ __launch_bounds__(512) void big_out_kernel(BigApplyParams p) {
   auto orow = [&](int blk) __attribute__((always_inline)) -> __bf16 * {
     return reinterpret_cast<__bf16 *>(blk == 0 ? st0 : blk == 1 ? st1 : blk == 2 ? st2 : st3);
   };
+  // tile (i, j) holds the products transposed: lane (g, li) has columns
+  // 128 wc + 16 j + 4 g + r of token row 16 i + li of the wave's 64-token block
   {
     __bf16 *os = orow(wr);
 #pragma unroll
     for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tr = 16 * i + 4 * g + r;        // row inside the wave's 64-token block
+      for (int j = 0; j < G::FN; ++j) {
+        bf16x4 v;
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j) os[st256(tr, wc * G::WN + 16 * j + li)] = (__bf16)acc[0][i][j][r];
+        for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[0][i][j][r];
+        *reinterpret_cast<bf16x4 *>(os + stage_w<G::TN>(16 * i + li, (wc * G::WN + 16 * j) / 4 + g)) = v;
       }
   }
   __syncthreads();
@@ -584,7 +597,7 @@ __global__ __launch_bounds__(512) void big_out_kernel(BigApplyParams p) {
     const int v = t + 512 * it;
     const int tr = v >> 5, cu = v & 31;           // 256 rows x 32 vectors
     const int64_t tok = tok0 + tr;
-    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(orow(it >> 2) + st256(tr & 63, 8 * cu));
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(orow(it >> 2) + stage_r<G::TN>(tr & 63, cu));
     if (tok < p.nq) __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(out + tok * p.ldo + 8 * cu));
   }
 }
