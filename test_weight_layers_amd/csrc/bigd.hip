@@ -35,6 +35,16 @@ __device__ __forceinline__ int64_t xcd_work_item(int64_t total) {
   return (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
 }
 
+// copy16_to_lds (global_load_lds_dwordx4) issued through inline asm, so that the
+// compiler does not count it: its waits for LDS reads cannot tell which stage a
+// pending copy writes once the copies stay in flight across a loop's back edge, and
+// it then waits for all of them.  The caller waits for these copies itself
+// (s_waitcnt vmcnt) before reading their data.
+__device__ __forceinline__ void copy16_to_lds_untracked(const void *gsrc, unsigned char *lds_wave_base) {
+  const unsigned m0v = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)lds_wave_base;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0v) : "memory");
+}
+
 // ------------------------------------------------------------------ NT tiles
 // C[i][j] = sum_k A[i][k] B[j][k], every operand row k-contiguous in HBM.  A
 // workgroup (WR x WC waves) stages NA "A" operands of TM rows and NB "B" operands

@@ -130,14 +130,6 @@ __device__ __forceinline__ void copy16_to_lds(const void *gsrc, unsigned char *l
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(gsrc),
                                    (__attribute__((address_space(3))) void *)(lds_wave_base), 16, 0, 0);
 }
-// The same copy issued through inline asm, so that the compiler does not count it:
-// its waits for LDS reads cannot tell which stage a pending copy writes when the
-// copies stay in flight across a loop's back edge, and it then waits for all of them.
-// The caller waits for these copies itself (s_waitcnt vmcnt) before reading their data.
-__device__ __forceinline__ void copy16_to_lds_untracked(const void *gsrc, unsigned char *lds_wave_base) {
-  const unsigned m0v = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)lds_wave_base;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0v) : "memory");
-}
 // buffer_load_dwordx4 ... lds: the same copy through a buffer view (wave-uniform base
 // and byte range in `rsrc`), each lane giving a 32-bit byte offset; fetches past the
 // range return zeros.  Keeps the per-lane address at one register instead of two.
