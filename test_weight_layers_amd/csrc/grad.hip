@@ -60,6 +60,20 @@ constexpr int kPkBytes = 4 * 3 * 64 * 16;
 typedef unsigned long long u64;
 typedef u64 u64x2 __attribute__((ext_vector_type(2)));
 
+// Buffer-view copies into LDS issued through inline asm, so that the compiler does
+// not count them (its waits cannot tell a copy in flight across the loop's back
+// edge from the stage being read, and it would wait for every copy).  The copying
+// waves wait for them with the explicit s_waitcnt in sync().  The leading s_nop 4
+// covers an SGPR operand written by a VALU instruction just before.
+__device__ __forceinline__ void copy16_untracked(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
+  const unsigned m0v = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)dst;
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0v) : "memory");
+}
+__device__ __forceinline__ void copy4_untracked(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
+  const unsigned m0v = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)dst;
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0v) : "memory");
+}
+
 // 4 kGradCS contraction waves: each takes two of the four hidden groups and
 // D / (2 kGradCS) of the output columns
 constexpr int kGradCS = 2;
@@ -111,9 +125,10 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
   // row r.  Contraction wave 4 + c (c < NDMA) copies K pieces c * PPW .. and the V
   // pieces of the same rows.  Rows past n are fetched from row n-1; their rate is 0,
   // which zeroes dH, dZ1, dZ3 and H' and so their whole contribution.
-  // Only the contraction waves DMA: the compiler cannot tell a pending DMA into one
-  // stage from the forward waves' plain LDS reads of another, and would make those
-  // reads wait for it.
+  // Only the contraction waves DMA (measured fastest: copies on the forward waves,
+  // which are the longer chain, slow the block down).  The copies are issued through
+  // inline asm that the compiler does not count (copy16_untracked), and sync() waits
+  // for them explicitly.
   constexpr int kRowsPer = 1024 / L::kRowBytes;           // token rows per 1 KB piece
   constexpr int NPIECE = 2 * L::kTile / 1024;             // K and V pieces per stage
   // four DMA waves, one per SIMD, so that the other contraction wave of each SIMD
@@ -141,8 +156,7 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     if (wv == 4) {
       const int valid = n - t0 < kTokBlock ? n - t0 : kTokBlock;
       const __amdgpu_buffer_rsrc_t er = buffer_view(eta + t0, 4u * (unsigned)valid);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void *)(dst + L::kEta), 4,
-                                               4u * (unsigned)l, 0, 0, 0);
+      copy4_untracked(er, 4u * (unsigned)l, dst + L::kEta);
     }
     auto piece_row = [&](int q) { return kRowsPer * (c * PPW + q) + l / L::kChunks; };
     // wave-uniform buffer views of the block's 32 rows; unsigned per-lane offsets
@@ -152,8 +166,8 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
 #pragma unroll
       for (int q = 0; q < PPW; ++q) {
         const int piece = c * PPW + q;
-        copy16_to_lds(kr, soff[q], dst + piece * 1024);
-        copy16_to_lds(vr, soff[q], dst + (piece + NPIECE / 2) * 1024);
+        copy16_untracked(kr, soff[q], dst + piece * 1024);
+        copy16_untracked(vr, soff[q], dst + (piece + NPIECE / 2) * 1024);
       }
     } else {                                                      // last block: clamp rows to n-1
 #pragma unroll
@@ -161,8 +175,8 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
         const int piece = c * PPW + q;
         const int r = piece_row(q), keep = n - 1 - t0;
         const unsigned off = r <= keep ? soff[q] : soff[q] - (unsigned)(r - keep) * row_bytes;
-        copy16_to_lds(kr, off, dst + piece * 1024);
-        copy16_to_lds(vr, off, dst + (piece + NPIECE / 2) * 1024);
+        copy16_untracked(kr, off, dst + piece * 1024);
+        copy16_untracked(vr, off, dst + (piece + NPIECE / 2) * 1024);
       }
     }
   };
@@ -353,8 +367,7 @@ __global__ __launch_bounds__((4 + 4 * CS) * 64, 1) void grad_fast_kernel(GradPar
     // iteration i: DMA of block i + 2 (stage (i + 2) % 4), contraction of block i - 1
     // (stage (i - 1) % 4, packed operands in buffer (i - 1) % 2).  Iteration 0 has no
     // contraction and runs before the loop, which then starts at i = 1.
-    // The packed operands are read before the DMA is issued: plain LDS reads after it
-    // would make the compiler wait for the DMA first.
+    // The packed operands are read before the DMA is issued.
     auto step = [&](int i, const unsigned char *ctr, unsigned char *dma, const unsigned char *pkr) {
       const bool issue = i + 2 < nb;
       bf16x8 pk1[2], pk3[2], pkh[2];
