@@ -50,7 +50,10 @@ __device__ __forceinline__ void copy16_to_lds_untracked(const void *gsrc, unsign
 // workgroup (WR x WC waves) stages NA "A" operands of TM rows and NB "B" operands
 // of TN rows, 32 reduction elements (64 bytes) per row, and multiplies NP (A, B)
 // pairs into NP accumulator sets.  Stages are DMA'd 1 KB (16 rows) per wave
-// instruction into a ring of NST stages, NST - 1 chunks ahead.
+// instruction into a ring of NST stages, NST - 1 chunks ahead.  Each MFMA takes the
+// B rows as its row operand, so the accumulator of 16 x 16 tile (i, j) holds C^T:
+// lane (g, li) has C[16 i + li][16 j + 4 g + r], r = 0..3 (four consecutive
+// columns of one row, which the epilogues store as one 8-byte unit).
 template <int NA_, int NB_, int TM_, int TN_, int NST_, int WR_ = 4, int WC_ = 2>
 struct NtGeo {
   static constexpr int NA = NA_, NB = NB_, TM = TM_, TN = TN_, NST = NST_, WR = WR_, WC = WC_;
