@@ -81,19 +81,21 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
   const char *wsrc[3] = {static_cast<const char *>(p.w1), static_cast<const char *>(p.w3),
                          static_cast<const char *>(p.w2t)};
   const int64_t head_off = (int64_t)h * p.m * D * 2;
-  auto stage_chunk = [&](int hc, unsigned char *dst) {
+  // piece q (of PPW) of this wave's share of chunk hc's copy into dst
+  auto stage_piece = [&](int hc, unsigned char *dst, int q) __attribute__((always_inline)) {
     const int64_t base = head_off + (int64_t)hc * kHidChunk * D * 2;   // wave-uniform
+    const int piece = w * PPW + q;
+    if (NPIECE % WV != 0 && piece >= NPIECE) return;     // wave-uniform
+    const int mat = piece / PPT, pr = piece % PPT;
+    const int r0 = kRowsPer * pr;
+    const unsigned s = 16u * (unsigned)((mat < 2 ? swz_rows_b128(r0) : swz_rows(r0)) & (L::kChunks - 1));
+    const __amdgpu_buffer_rsrc_t rs = buffer_view(wsrc[mat] + base, L::kTile);
+    copy16_to_lds(rs, xor_scalar_here(mat < 2 ? lane_b128 : lane_rows, s), 1024u * (unsigned)pr,
+                  dst + piece * 1024);
+  };
+  auto stage_chunk = [&](int hc, unsigned char *dst) {
 #pragma unroll
-    for (int q = 0; q < PPW; ++q) {
-      const int piece = w * PPW + q;
-      if (NPIECE % WV != 0 && piece >= NPIECE) break;     // wave-uniform
-      const int mat = piece / PPT, pr = piece % PPT;
-      const int r0 = kRowsPer * pr;
-      const unsigned s = 16u * (unsigned)((mat < 2 ? swz_rows_b128(r0) : swz_rows(r0)) & (L::kChunks - 1));
-      const __amdgpu_buffer_rsrc_t rs = buffer_view(wsrc[mat] + base, L::kTile);
-      copy16_to_lds(rs, xor_scalar_here(mat < 2 ? lane_b128 : lane_rows, s), 1024u * (unsigned)pr,
-                    dst + piece * 1024);
-    }
+    for (int q = 0; q < PPW; ++q) stage_piece(hc, dst, q);
   };
 
   // W1 / W3 reads: row perm_row(u, li), chunk 4kc + g  ->  base ^ 64 kc
@@ -157,8 +159,9 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
     }
   };
   // O^T[d][tok] += W2[d][chunk] H^T for the chunk staged at `base`; the transposing
-  // reads run kRing column blocks ahead of their MFMAs.
-  auto second = [&](const unsigned char *base, const bf16x4(&h0)[2], const bf16x4(&h1)[2])
+  // reads run kRing column blocks ahead of their MFMAs, and between(dt) runs after
+  // column block dt's products.
+  auto second = [&](const unsigned char *base, const bf16x4(&h0)[2], const bf16x4(&h1)[2], auto &&between)
                     __attribute__((always_inline)) {
     const bf16x8 hf0 = cat8(h0[0], h1[0]), hf1 = cat8(h0[1], h1[1]);
     constexpr int kRing = 6;
@@ -175,6 +178,7 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
       const bf16x8 w2f = cat8(wlo[dt % kRing], whi[dt % kRing]);
       acc[dt][0] = mma(w2f, hf0, acc[dt][0]);
       acc[dt][1] = mma(w2f, hf1, acc[dt][1]);
+      between(dt);
     }
   };
 
@@ -182,7 +186,9 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
   //   A: first product of half 0 of chunk c, hiding the gate of half 1 of chunk c - 1;
   //   B: the second product of chunk c - 1 (its W2^T still in the previous stage);
   //   C: first product of half 1 of chunk c, hiding the gate of half 0 of chunk c;
-  // and the DMA of chunk c + 1 into the stage chunk c - 2 left.
+  // and the DMA of chunk c + 1 into the stage chunk c - 2 left, its copies spread over
+  // B's products (issued all at the start of A, they held both waves of a SIMD at
+  // once: 2% slower).
   const int nch = p.m / kHidChunk;
   f32x4 za1[2], za3[2];   // half 0 of chunk c (made in A, gated in C)
   f32x4 zb1[2], zb3[2];   // half 1 of chunk c (made in C, gated in A of the next chunk)
@@ -190,9 +196,14 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
   auto no_gate = [](int) __attribute__((always_inline)) {};
   auto iter = [&](int c, const unsigned char *cur, const unsigned char *prev, unsigned char *next)
                   __attribute__((always_inline)) {
-    if (c + 1 < nch) stage_chunk(c + 1, next);
+    const bool more = c + 1 < nch;
     first_half(cur, 0, za1, za3, [&](int kc) __attribute__((always_inline)) { gate_part(kc, zb1, zb3, h1); });
-    second(prev, h0, h1);
+    // the copies of chunk c + 1 go out spread over the second product
+    second(prev, h0, h1, [&](int dt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < PPW; ++q)
+        if (more && q * DT / PPW == dt) stage_piece(c + 1, next, q);
+    });
     first_half(cur, 1, zb1, zb3, [&](int kc) __attribute__((always_inline)) { gate_part(kc, za1, za3, h0); });
     wait_all_memory();
     __syncthreads();
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(64 * WV, 1) void apply_fast_kernel(ApplyParams p) {
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) gate_part(kc, zb1, zb3, h1);
   const int last = (nch - 1) % 3;
-  second(last == 0 ? sa : last == 1 ? sb : sc, h0, h1);
+  second(last == 0 ? sa : last == 1 ? sb : sc, h0, h1, [](int) __attribute__((always_inline)) {});
 
   // O goes out through LDS: each wave writes its 32 x D bf16 tile (row = token) into a
   // region of its own, then stores whole rows with 16-byte lanes (every store
