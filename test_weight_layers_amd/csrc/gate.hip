@@ -144,8 +144,16 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
     for (int e = 0; e < 8; ++e) acc[a][e] = f32x4{0, 0, 0, 0};
   float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const unsigned char *stage) __attribute__((always_inline)) {
-    if (!active) return;
+  // copy j (of kDma) of this wave's share of chunk kc into dst
+  auto issue_one = [&](int kc, unsigned char *dst, int j) __attribute__((always_inline)) {
+    const unsigned kb = (unsigned)kc * G::kRowB;
+    if (j < G::kDmaA)
+      copy16_to_lds(arsrc, aoff[j], kb, dst + (G::kDmaA * w + j) * 1024);
+    else
+      copy16_to_lds(brsrc, boff[j - G::kDmaA], kb, dst + G::kStageA + (G::kDmaB * w + j - G::kDmaA) * 1024);
+  };
+  // products of the stage; between(e) runs after column tile e of the first k-step
+  auto compute = [&](const unsigned char *stage, auto &&between) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < G::kKs; ++ks) {
       typename FragOf<T>::type fa[4];
@@ -156,6 +164,7 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
         const typename FragOf<T>::type fb = gate_frag<T>(stage + G::kStageA, 128 * wc + 16 * e + li, ks, g);
 #pragma unroll
         for (int a = 0; a < 4; ++a) acc[a][e] = mma(fa[a], fb, acc[a][e]);
+        if (ks == 0) between(e);
       }
       if (wc == 0) {
 #pragma unroll
@@ -165,7 +174,9 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
   };
   const int nk = C / G::kEpc;
   // one chunk: wait for its stage (the later chunks' DMAs may stay in flight),
-  // barrier, refill the stage read one chunk ago with chunk kc + NST - 1, multiply
+  // barrier, multiply, refilling the stage read one chunk ago with chunk kc + NST - 1
+  // (its copies spread over the first k-step's column tiles: issued all after the
+  // barrier they held every wave at once, 4% slower)
   auto step = [&](int kc, const unsigned char *cur, unsigned char *refill) __attribute__((always_inline)) {
     const int later = nk - 1 - kc;                // chunks after kc already issued: min(later, NST - 2)
     if (NST > 3 && later >= 2)
@@ -175,8 +186,17 @@ __global__ __launch_bounds__(512) void gate_kernel(GateParams p) {
     else
       wait_vmcnt<0>();
     bare_barrier();
-    if (kc + NST - 1 < nk) issue(kc + NST - 1, refill);
-    compute(cur);
+    const bool more = kc + NST - 1 < nk;          // wave-uniform
+    if (!active) {                                // no products: copy at once
+      if (more) issue(kc + NST - 1, refill);
+      return;
+    }
+    // the copies of chunk kc + NST - 1 go out spread over the first k-step's column tiles
+    compute(cur, [&](int e) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < G::kDma; ++j)
+        if (more && j * 8 / G::kDma == e) issue_one(kc + NST - 1, refill, j);
+    });
   };
   unsigned char *const ring[4] = {st0, st1, st2, st3};
 #pragma unroll
