@@ -227,6 +227,31 @@ def test_shortconv2d_against_oracle(dtype):
     assert torch.equal(got[sp].cpu(), inp.v[sp])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("grid_h,grid_w,n_special,channels", [
+    (1, 1, 0, 64), (3, 2, 2, 128), (5, 7, 1, 192), (2, 63, 3, 64), (4, 64, 1, 64), (3, 5, 2, 72)])
+def test_shortconv2d_grids(dtype, grid_h, grid_w, n_special, channels):
+    # edge geometries: one-row and one-column grids, no special tokens, odd widths,
+    # wide grids, and channel counts that are not a multiple of 64
+    from test_weight_layers_amd import ttt
+    frames, tpf = 3, n_special + grid_h * grid_w
+    rng = np.random.default_rng(7 + grid_w)
+    v = torch.from_numpy(rng.standard_normal((frames * tpf, channels)).astype(np.float32))
+    v = v.to(torch.bfloat16) if dtype == "bf16" else v
+    wconv = torch.from_numpy((0.1 * rng.standard_normal((channels, 3, 3))).astype(np.float32))
+    geo = dict(frames=frames, tokens_per_frame=tpf, n_special=n_special, grid_h=grid_h, grid_w=grid_w)
+    got = ttt.shortconv2d(v.cuda(), wconv.cuda(), **geo)
+    torch.cuda.synchronize()
+    ref = oracle.shortconv2d(synth.as_f64(v), synth.as_f64(wconv), **geo)
+    g = got.double().cpu().numpy()
+    if dtype == "f32":
+        np.testing.assert_allclose(g, ref, rtol=1e-5, atol=1e-6)
+    else:
+        np.testing.assert_allclose(g, ref, rtol=2 ** -8, atol=1e-6)
+    sp = np.concatenate([np.arange(f * tpf, f * tpf + n_special) for f in range(frames)]).astype(np.int64)
+    assert torch.equal(got[sp].cpu(), v[sp])
+
+
 @pytest.mark.parametrize("kind", ["bf16-fast", "f32", "bf16-d768"])
 def test_stream_against_oracle(kind):
     # the stream carries each chunk's operand copies to the next chunk; covered for
